@@ -1,0 +1,124 @@
+/*
+ * monarch_attn.h -- C ABI of the MI355X (gfx950) Monarch-factored video attention library.
+ *
+ * Operation. For a video token grid (T, H, W) flattened as n = (t*H + h)*W + w,
+ * the attention matrix is taken as a product of permutation and block-diagonal
+ * factors, M = P . blockdiag(L_0..L_{b2-1}) . P^T . blockdiag(R_0..R_{b1-1})
+ * (MonarchRT summaries, nl page "Methodologie"; P a permutation: zh page 2.1),
+ * with blocks aligned to whole grid axes, (b1, b2) = (T*H, W) and b1*b2 = N
+ * (zh page 2.2, "block alignment"). The library computes O = M V with
+ *   stage R: Y[a*b2+i] = sum_j softmax_j(s q_{a*b2+i} . k_{a*b2+j}) v_{a*b2+j}
+ *            (softmax attention inside each block of b2 contiguous tokens),
+ *   stage L: O[a*b2+i] = sum_c softmax_c(s q_{a*b2+i} . k_{c*b2+i}) Y[c*b2+i]
+ *            (softmax attention among the b1 tokens that share intra-block
+ *            index i; the stride permutation P is applied by addressing only),
+ * s = 1/sqrt(head_dim), the original Q and K in both stages, R applied first.
+ * Tiled Monarch (zh page 2.2 "Tiled Monarch"; fr page 2.B; nl "Methodologie")
+ * restricts each stage-L softmax to a box of tile_t frames x tile_h rows at a
+ * fixed w; the last box on an axis may be shorter.
+ *
+ * Tensors. q, k, v, out (and the workspace) are dense row-major
+ * [batch, heads, N, head_dim] arrays of one dtype (MA_BF16 or MA_F32), head_dim
+ * fastest, N = T*H*W. All pointers are caller-owned DEVICE pointers, 16-byte
+ * aligned. The library allocates nothing, keeps no state between calls, and is
+ * reentrant; work is enqueued on `stream` (NULL = the default stream) and every
+ * call returns without synchronizing. bf16 inputs are accumulated in fp32; the
+ * stage-R intermediate Y is stored in the input dtype.
+ *
+ * Errors. Every argument is checked on the host before any HIP call; a failed
+ * check returns a negative ma_status and enqueues nothing. A zero-sized problem
+ * (batch, heads or a grid axis equal to 0) is a no-op returning MA_OK. A HIP
+ * launch failure returns MA_ERR_HIP (details: ma_last_hip_error()).
+ */
+#ifndef MONARCH_ATTN_H_
+#define MONARCH_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t *` */
+
+typedef enum {
+  MA_OK = 0,
+  MA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad r_axes or tile, aliasing */
+  MA_ERR_UNSUPPORTED = -2,  /* head_dim not in {16,32,64,128}, dtype unknown, size limits */
+  MA_ERR_ALIGNMENT = -3,    /* a pointer is not 16-byte aligned */
+  MA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than ma_workspace_bytes() */
+  MA_ERR_HIP = -5           /* the HIP runtime rejected a launch */
+} ma_status;
+
+typedef enum { MA_BF16 = 0, MA_F32 = 1 } ma_dtype;
+
+/* Block spec `r_axes`: how many trailing grid axes form one stage-R block.
+ *   1: b2 = W,     b1 = T*H  (the aligned (f*h, w) split; the default)
+ *   2: b2 = H*W,   b1 = T    (the aligned (f, h*w) split)
+ *   3: b2 = N,     b1 = 1    (one block: plain dense attention, stage L skipped)
+ *   0: b2 = 1,     b1 = N    (stage R skipped: plain dense attention through stage L) */
+
+/* Bytes of workspace (the stage-R output Y) that monarch_attn_fwd /
+ * monarch_attn_tiled_fwd need for this problem; 0 when one stage is trivial and
+ * Y is written straight to `out` or read straight from `v`. Returns 0 for
+ * invalid arguments too (the entry points then report the error). */
+size_t ma_workspace_bytes(int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                          int32_t r_axes, int32_t tile_t, int32_t tile_h,
+                          int32_t head_dim, int32_t dtype);
+
+/* Monarch attention, untiled: O = P L P^T R V as defined above.
+ * workspace: device buffer of at least ma_workspace_bytes(...) bytes (may be
+ * NULL when that is 0); it must not overlap q, k, v or out. out must not
+ * overlap q, k, v. */
+int monarch_attn_fwd(const void *q, const void *k, const void *v, void *out,
+                     void *workspace, size_t workspace_bytes,
+                     int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                     int32_t r_axes, int32_t head_dim, int32_t dtype,
+                     struct ihipStream_t *stream);
+
+/* Tiled Monarch attention: as monarch_attn_fwd with r_axes = 1, but each
+ * stage-L softmax runs only over the box {(t', h') : t'/tile_t = t/tile_t,
+ * h'/tile_h = h/tile_h} at the same w. tile_t, tile_h >= 1; tiles larger than
+ * the grid clamp to it (tile (T, H) equals the untiled operator; tile (1, 1)
+ * makes stage L the identity, so O = Y). */
+int monarch_attn_tiled_fwd(const void *q, const void *k, const void *v, void *out,
+                           void *workspace, size_t workspace_bytes,
+                           int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                           int32_t tile_t, int32_t tile_h, int32_t head_dim, int32_t dtype,
+                           struct ihipStream_t *stream);
+
+/* Dense comparator: O = softmax(s Q K^T) V over all n_tokens, per (batch, head)
+ * (the quadratic 3D self-attention the method replaces: it page 1, zh overview).
+ * out must not overlap q, k, v. */
+int dense_attn_fwd(const void *q, const void *k, const void *v, void *out,
+                   int32_t batch, int32_t heads, int32_t n_tokens, int32_t head_dim,
+                   int32_t dtype, struct ihipStream_t *stream);
+
+/* The two stages as separate calls (same definitions; used to time and test
+ * each kernel on its own).
+ * ma_stage_r_fwd writes Y = blockdiag(R) V into y (same shape as v).
+ * ma_stage_l_fwd reads Y from y and writes O = P L P^T Y into out; tile_t =
+ * tile_h = 0 selects the untiled stage L, otherwise tiles need r_axes = 1.
+ * y must not overlap q, k, v (stage R) or q, k, out (stage L). */
+int ma_stage_r_fwd(const void *q, const void *k, const void *v, void *y,
+                   int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                   int32_t r_axes, int32_t head_dim, int32_t dtype,
+                   struct ihipStream_t *stream);
+int ma_stage_l_fwd(const void *q, const void *k, const void *y, void *out,
+                   int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                   int32_t r_axes, int32_t tile_t, int32_t tile_h,
+                   int32_t head_dim, int32_t dtype, struct ihipStream_t *stream);
+
+/* Static text for a status code (never NULL). */
+const char *ma_status_string(int status);
+
+/* The hipError_t value behind the last MA_ERR_HIP returned on this thread
+ * (0 if none). */
+int ma_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MONARCH_ATTN_H_ */

@@ -1,0 +1,25 @@
+// kernels_common.h -- launch arguments and small device helpers shared by the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "group_addr.h"
+
+namespace ma {
+
+// One launch runs softmax attention independently inside every token group
+// of every (batch, head): out[g] = softmax(s q[g] k[g]^T) vals[g].
+struct AttnLaunch {
+  const void *q;
+  const void *k;
+  const void *vals;   // V (stage R, dense) or Y (stage L)
+  void *out;
+  int64_t head_elems; // N * head_dim: distance between consecutive (batch, head) slices
+  GroupAddr ga;
+  int32_t n_qtiles;   // query tiles per group (sized for the largest group)
+  int32_t n_bh;       // batch * heads
+  float scale;        // 1/sqrt(head_dim)
+  float scale_log2;   // scale * log2(e): softmax evaluated with exp2
+};
+
+}  // namespace ma

@@ -1,0 +1,187 @@
+"""CPU tests of the C ABI: symbols, argument checks, error codes and group addressing.
+
+Nothing here launches a kernel. Every call below either fails an argument
+check (which the library performs before any HIP call) or describes an empty
+problem; the group addressing is exercised through a host-only build of the
+library's own headers (tests/host/group_enum.cpp).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "monarch_attn.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from structured_attention_video_attn_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from structured_attention_video_attn_amd import build
+        build.build()
+    return _binding.load_library()
+
+
+@pytest.fixture(scope="module")
+def group_enum(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("host") / "group_enum")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-o", exe,
+                    os.path.join(ROOT, "tests", "host", "group_enum.cpp")], check=True)
+    return exe
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert set(names) >= {"monarch_attn_fwd", "monarch_attn_tiled_fwd", "dense_attn_fwd",
+                          "ma_workspace_bytes", "ma_status_string", "ma_stage_r_fwd",
+                          "ma_stage_l_fwd", "ma_last_hip_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5, 17):
+        s = lib.ma_status_string(st)
+        assert s is not None and len(s) > 0
+    assert lib.ma_status_string(-4).startswith(b"MA_ERR_WORKSPACE")
+    assert lib.ma_last_hip_error() == 0
+
+
+def test_workspace_bytes(lib):
+    ws = lib.ma_workspace_bytes
+    assert ws(1, 12, 21, 30, 52, 1, 0, 0, 128, BF16) == 12 * 32760 * 128 * 2
+    assert ws(2, 3, 2, 4, 4, 1, 0, 0, 16, F32) == 2 * 3 * 32 * 16 * 4
+    assert ws(1, 12, 21, 30, 52, 1, 3, 30, 128, BF16) == 12 * 32760 * 128 * 2
+    assert ws(1, 1, 2, 4, 4, 3, 0, 0, 16, F32) == 0      # one block: Y goes straight to out
+    assert ws(1, 1, 2, 4, 4, 0, 0, 0, 16, F32) == 0      # b2 = 1: stage L reads V
+    assert ws(1, 1, 2, 4, 4, 1, 1, 1, 16, F32) == 0      # 1x1 tiles: stage L is the identity
+    assert ws(1, 1, 2, 4, 4, 1, 0, 0, 48, F32) == 0      # unsupported head_dim
+    assert ws(0, 1, 2, 4, 4, 1, 0, 0, 16, F32) == 0      # empty
+
+
+A16 = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
+BIG = 1 << 30
+
+
+def _ptrs(n=5, stride=BIG):
+    return [A16 + i * stride for i in range(n)]
+
+
+def test_monarch_argument_errors(lib):
+    f = lib.monarch_attn_fwd
+    q, k, v, o, w = _ptrs()
+    nb = 12 * 32760 * 128 * 2
+    good = dict(batch=1, heads=12, T=21, H=30, W=52, r=1, d=128, dt=BF16)
+
+    def call(q=q, k=k, v=v, o=o, w=w, wb=nb, **kw):
+        a = dict(good, **kw)
+        return f(q, k, v, o, w, wb, a["batch"], a["heads"], a["T"], a["H"], a["W"], a["r"], a["d"],
+                 a["dt"], None)
+
+    assert call(q=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(heads=-3) == INVALID
+    assert call(r=4) == INVALID
+    assert call(r=-1) == INVALID
+    assert call(d=48) == UNSUPPORTED
+    assert call(d=256) == UNSUPPORTED
+    assert call(dt=7) == UNSUPPORTED
+    assert call(q=A16 + 8) == ALIGN
+    assert call(o=A16 + 4 * BIG + 2) == ALIGN
+    assert call(w=None) == WORKSPACE
+    assert call(wb=nb - 1) == WORKSPACE
+    assert call(w=A16 + 4 * BIG + 8) == ALIGN
+    assert call(o=q) == INVALID                     # out aliases q
+    assert call(o=k + 4096) == INVALID              # out overlaps k
+    assert call(w=v) == INVALID                     # workspace aliases v
+    assert call(w=o + 2 * 16) == INVALID            # workspace overlaps out
+    assert call(T=1 << 20, H=1 << 10, W=1) == UNSUPPORTED   # N*d beyond 32-bit offsets
+    # empty problems are no-ops, even with null pointers
+    assert call(q=None, k=None, v=None, o=None, w=None, batch=0) == OK
+    assert call(q=None, k=None, v=None, o=None, w=None, W=0) == OK
+
+
+def test_tiled_and_stage_argument_errors(lib):
+    q, k, v, o, w = _ptrs()
+    nb = 1 << 28
+    t = lib.monarch_attn_tiled_fwd
+    assert t(q, k, v, o, w, nb, 1, 12, 21, 30, 52, 0, 30, 128, BF16, None) == INVALID
+    assert t(q, k, v, o, w, nb, 1, 12, 21, 30, 52, 3, -1, 128, BF16, None) == INVALID
+    assert t(q, k, v, o, None, 0, 1, 12, 21, 30, 52, 3, 30, 128, BF16, None) == WORKSPACE
+    assert t(q, k, v, q, w, nb, 1, 12, 21, 30, 52, 3, 30, 128, BF16, None) == INVALID
+    assert t(q, k, v, o, w, nb, 1, 12, 21, 30, 52, 3, 30, 24, BF16, None) == UNSUPPORTED
+    assert t(None, None, None, None, None, 0, 1, 0, 21, 30, 52, 3, 30, 128, BF16, None) == OK
+    r = lib.ma_stage_r_fwd
+    assert r(q, k, v, q, 1, 12, 21, 30, 52, 1, 128, BF16, None) == INVALID
+    assert r(q, k, v, o, 1, 12, 21, 30, 52, 7, 128, BF16, None) == INVALID
+    assert r(q, k, v, o + 8, 1, 12, 21, 30, 52, 1, 128, BF16, None) == ALIGN
+    l = lib.ma_stage_l_fwd
+    assert l(q, k, v, o, 1, 12, 21, 30, 52, 2, 3, 30, 128, BF16, None) == INVALID  # tiles need r_axes 1
+    assert l(q, k, v, o, 1, 12, 21, 30, 52, 1, 3, 0, 128, BF16, None) == INVALID
+    assert l(q, k, o, o, 1, 12, 21, 30, 52, 1, 0, 0, 128, BF16, None) == INVALID   # out aliases y
+    d = lib.dense_attn_fwd
+    assert d(q, k, v, None, 1, 12, 4680, 128, BF16, None) == INVALID
+    assert d(q, k, v, o, 1, 12, -5, 128, BF16, None) == INVALID
+    assert d(q, k, v, o, 1, 12, 4680, 100, BF16, None) == UNSUPPORTED
+    assert d(q, k, v, v, 1, 12, 4680, 128, BF16, None) == INVALID
+    assert d(None, None, None, None, 1, 12, 0, 128, BF16, None) == OK
+
+
+def _parse_groups(text):
+    r, l = [], []
+    lines = text.strip().splitlines()
+    trivial = tuple(int(x) for x in lines[0].split()[1:])
+    for line in lines[1:]:
+        tag, rest = line.split(" ", 1)
+        toks = [int(x) for x in rest.split(":")[1].split()]
+        (r if tag == "R" else l).append(frozenset(toks))
+    return trivial, r, l
+
+
+GRIDS = [
+    ((2, 4, 4), 1, None), ((2, 4, 4), 2, None), ((2, 4, 4), 3, None), ((2, 4, 4), 0, None),
+    ((3, 5, 7), 1, None), ((3, 5, 7), 1, (2, 2)), ((3, 5, 7), 1, (1, 5)), ((3, 5, 7), 1, (3, 1)),
+    ((3, 5, 7), 1, (4, 9)), ((4, 3, 2), 1, (3, 2)), ((2, 4, 4), 1, (1, 2)), ((7, 6, 5), 1, (3, 4)),
+    ((3, 30, 52), 1, None), ((21, 30, 52), 1, (3, 30)), ((5, 7, 3), 2, None),
+]
+
+
+@pytest.mark.parametrize("grid,r_axes,tile", GRIDS)
+def test_group_addressing_matches_oracle(group_enum, grid, r_axes, tile):
+    T, H, W = grid
+    tt, th = tile if tile else (0, 0)
+    out = subprocess.run([group_enum, "groups", str(T), str(H), str(W), str(r_axes), str(tt), str(th)],
+                         capture_output=True, text=True, check=True).stdout
+    (r_triv, l_triv), r_groups, l_groups = _parse_groups(out)
+    want_r = [frozenset(g.tolist()) for g in oracle.stage_r_groups(grid, r_axes)]
+    want_l = [frozenset(g.tolist()) for g in oracle.stage_l_groups(grid, r_axes, tile)]
+    assert sorted(map(sorted, r_groups)) == sorted(map(sorted, want_r))
+    assert sorted(map(sorted, l_groups)) == sorted(map(sorted, want_l))
+    assert r_triv == int(all(len(g) == 1 for g in want_r))
+    assert l_triv == int(all(len(g) == 1 for g in want_l))
+
+
+def test_xcd_remap_is_bijective(group_enum):
+    out = subprocess.run([group_enum, "remap", "4100"], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "ok"
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from structured_attention_video_attn_amd import _binding
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.load_library(str(tmp_path / "missing.so"))
