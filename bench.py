@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark: Monarch-factored video attention forward on one MI355X.
+
+One step = one ``monarch_attn_fwd`` call (stage R + stage L) over the
+21x30x52 token grid (32760 tokens), batch 1, 12 heads, head_dim 128, bf16,
+on seeded synthetic Q/K/V (Q, K ~ N(0,1)/128^0.25, V ~ N(0,1)). The timed
+region rotates over several input/output buffer sets (together larger than
+the 256 MB MALL) so that every step reads its inputs from HBM.
+
+Printed as one JSON line: tokens/s and ms/step of that step, the roofline
+of the dominant kernel (timed with HIP events on the launch stream inside the
+timed loop), the whole step against its two-stage roofline, side figures
+(warm-cache step, tiled Monarch on structured data, the dense comparator),
+and the CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "Monarch-attn ms/call & tokens/s at 21×30×52 grid, 12h d128; % HBM/MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_stage_l.json")
+KERNEL_SOURCES = ["attn_bf16.h", "group_addr.h", "kernels_common.h", "monarch_attn.hip"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets in the timed loop")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip tiled/dense side figures")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "structured_attention_video_attn_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stage_work(N, d, heads, group_len):
+    """(flops, compulsory bytes) of one stage over groups of `group_len` tokens (bf16)."""
+    flops = 4.0 * N * d * heads * group_len
+    nbytes = 8.0 * N * d * heads          # read Q, K, V-or-Y; write Y-or-O (2 B each)
+    return flops, nbytes
+
+
+def roofline_us(flops, nbytes):
+    return max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(wl, q, k, v):
+    """The fp64 oracle, as it stands, on the host cores: whole 12-head calls."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    grid = (wl.T, wl.H, wl.W)
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.monarch_attention(q, k, v, grid)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or calls >= 5:
+            break
+    return {"value": wl.n_tokens * calls / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole call(s) of the fp64 NumPy oracle at 21x30x52, 12 heads, d128 "
+                      "(stage R + stage L), %.1f s wall" % (calls, el)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the method is measured on a single MI355X and "
+              "this build has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import structured_attention_video_attn_amd as ma
+    from workloads import WORKLOADS, make_qkv
+
+    ma.load_library()   # raises when the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = WORKLOADS["full"]
+    T, H, W = wl.T, wl.H, wl.W
+    N, d, heads = wl.n_tokens, wl.head_dim, wl.heads
+    q_np, k_np, v_np = make_qkv(wl)
+    up = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    base = [up(x) for x in (q_np, k_np, v_np)]
+    ws_elems = ma.ma_workspace_bytes(1, heads, T, H, W, 1, 0, 0, d, ma.MA_BF16) // 2
+    sets = []
+    for s in range(max(1, args.sets)):
+        q, k, v = (x.clone() for x in base)
+        sets.append((q, k, v, torch.empty_like(q), torch.empty(ws_elems, dtype=torch.bfloat16, device=dev)))
+    del base
+    torch.cuda.synchronize()
+
+    def step(i):
+        q, k, v, o, ws = sets[i % len(sets)]
+        ma.monarch_attn_fwd(q, k, v, o, ws, T, H, W)
+
+    ms = time_loop(step, args.steps, args.warmup)
+    ms_warm = time_loop(lambda i: step(0), args.steps, args.warmup)
+
+    # Per-kernel durations, live, with events on the stream the kernels run on.
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        q, k, v, o, ws = sets[i % len(sets)]
+        y = ws.view(q.shape)
+        ev[i][0].record(stream)
+        ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
+        ev[i][1].record(stream)
+        ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    r_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    l_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+
+    fr, br = stage_work(N, d, heads, W)
+    fl, bl = stage_work(N, d, heads, T * H)
+    roof_r, roof_l = roofline_us(fr, br), roofline_us(fl, bl)
+    if l_us >= r_us:
+        name, dur, f, b = "stage_l", l_us, fl, bl
+    else:
+        name, dur, f, b = "stage_r", r_us, fr, br
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma_bound = f / b >= ridge
+    achieved = (f / (dur * 1e-6) / 1e12) if mfma_bound else (b / (dur * 1e-6) / 1e9)
+    peak = PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("kernel") == name:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": name,
+                "kernel_us": round(dur, 2), "algorithmic_flops": f, "algorithmic_bytes": b}
+
+    extras = {}
+    if not args.no_extras:
+        wl3 = WORKLOADS["structured"]
+        q3, k3, v3 = (up(x) for x in make_qkv(wl3))
+        o3 = torch.empty_like(q3)
+        ws3 = torch.empty(ws_elems, dtype=torch.bfloat16, device=dev)
+        tt, th = wl3.tile
+        ms_tiled = time_loop(lambda i: ma.monarch_attn_tiled_fwd(q3, k3, v3, o3, ws3, T, H, W, tt, th),
+                             args.steps, args.warmup)
+        del q3, k3, v3, o3, ws3
+        q, k, v, o, _ = sets[0]
+        ms_dense = time_loop(lambda i: ma.dense_attn_fwd(q, k, v, o), 3, 1)
+        fr3, br3 = stage_work(N, d, heads, W)
+        fl3, bl3 = stage_work(N, d, heads, tt * th)
+        extras = {
+            "tiled_structured_ms": round(ms_tiled, 4),
+            "tiled_structured_tokens_per_s": round(N / (ms_tiled * 1e-3), 1),
+            "tiled_structured_roofline_frac": round(
+                (roofline_us(fr3, br3) + roofline_us(fl3, bl3)) / (ms_tiled * 1e3), 4),
+            "dense_ms": round(ms_dense, 3),
+            "dense_tflops": round(4.0 * N * N * d * heads / (ms_dense * 1e-3) / 1e12, 1),
+            "monarch_speedup_vs_dense": round(ms_dense / ms, 2),
+        }
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q,K/128^0.25 and V; rotating buffer sets, inputs in HBM)",
+        "config": {"workload": "monarch_attn_fwd 21x30x52 grid (32760 tokens), batch 1, 12 heads, "
+                               "head_dim 128, blocks (b1,b2)=(630,52)",
+                   "T": T, "H": H, "W": W, "batch": 1, "heads": heads, "head_dim": d,
+                   "buffer_sets": len(sets)},
+        "roofline": roofline,
+        "step_roofline": {"roofline_us": round(roof_r + roof_l, 2), "measured_us": round(ms * 1e3, 2),
+                          "frac": round((roof_r + roof_l) / (ms * 1e3), 4),
+                          "stage_r_us": round(r_us, 2), "stage_l_us": round(l_us, 2)},
+        "warm_ms_per_step": round(ms_warm, 5),
+    }
+    out.update(extras)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, q_np, k_np, v_np)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,10 +31,10 @@ template <int D>
 int launch_d(const AttnLaunch &a, int nw, uint32_t blocks, hipStream_t s) {
   if (nw == 0) {
     hipLaunchKernelGGL(group_attn_f32<D>, dim3(blocks), dim3(kF32Threads), 0, s, a);
-  } else if (nw == 2) {
-    hipLaunchKernelGGL((group_attn_bf16<D, 2>), dim3(blocks), dim3(128), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((group_attn_bf16<D, 4>), dim3(blocks), dim3(256), 0, s, a);
+  } else if (nw == 2) {   // groups of at most 64 tokens: one key tile
+    hipLaunchKernelGGL((group_attn_bf16<D, 2, 1>), dim3(blocks), dim3(128), 0, s, a);
+  } else {                 // longer groups: double-buffered key/value tiles
+    hipLaunchKernelGGL((group_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, s, a);
   }
   return hip_status(hipGetLastError());
 }
