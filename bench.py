@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "Monarch-attn ms/call & tokens/s at 21×30×52 grid, 12h d128; % HBM/MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_stage_l.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_%s.json")
 KERNEL_SOURCES = ["attn_bf16.h", "group_addr.h", "kernels_common.h", "monarch_attn.hip"]
 
 
@@ -42,6 +42,16 @@ def parse_args():
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets in the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip tiled/dense side figures")
+    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy"],
+                    help="run only this kernel (or a plain device copy of one input tensor, the "
+                         "calibration for byte counters) --steps times on the 21x30x52 workload; "
+                         "for counter collection under rocprofv3")
+    ap.add_argument("--summarize-counters", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output (kernel runs and "
+                         "copy runs) into the per-launch HBM traffic of --kernel, written to "
+                         "profiles/traffic_full_<kernel>.json")
+    ap.add_argument("--kernel", default="stage_l", choices=["stage_l", "stage_r"])
     return ap.parse_args()
 
 
@@ -102,8 +112,88 @@ def cpu_baseline(wl, q, k, v):
                       "(stage R + stage L), %.1f s wall" % (calls, el)}
 
 
+KERNEL_SYMBOL = {"stage_l": "group_attn_bf16", "stage_r": "block_attn_bf16"}
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel):
+    """Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a device copy of one 100.6 MB tensor."""
+    wl_bytes = 12 * 32760 * 128 * 2
+    sym = KERNEL_SYMBOL[kernel]
+
+    def mean_for(rows, pred):
+        vals = [v for name, v in rows if pred(name)]
+        if not vals:
+            raise SystemExit("no matching dispatches in counter output")
+        return sum(vals) / len(vals)
+
+    copy_pred = lambda name: "copyBuffer" in name   # device-to-device copies only
+    fetch_scale = wl_bytes / (1024.0 * mean_for(_counter_rows(copy_fetch_dir, "FETCH_SIZE"), copy_pred))
+    write_scale = wl_bytes / (1024.0 * mean_for(_counter_rows(copy_write_dir, "WRITE_SIZE"), copy_pred))
+    kpred = lambda name: sym in name
+    fetch = 1024.0 * mean_for(_counter_rows(fetch_dir, "FETCH_SIZE"), kpred) * fetch_scale
+    write = 1024.0 * mean_for(_counter_rows(write_dir, "WRITE_SIZE"), kpred) * write_scale
+    out = {"kernel": kernel, "kernel_symbol": sym, "kernel_source_hash": kernel_source_hash(),
+           "fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "algorithmic_bytes": 8.0 * 32760 * 128 * 12}
+    path = os.path.join(ROOT, "profiles", "traffic_full_%s.json" % kernel)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def profile_only(which, steps, n_sets=3):
+    """Run one kernel `steps` times over rotating buffer sets (about 1.5 GB in all,
+    more than the 256 MB MALL), so that every launch reads its inputs from HBM."""
+    import torch
+    import structured_attention_video_attn_amd as ma
+    from workloads import WORKLOADS, make_qkv
+    ma.load_library()
+    wl = WORKLOADS["full"]
+    T, H, W = wl.T, wl.H, wl.W
+    dev = torch.device("cuda:0")
+    base = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in make_qkv(wl)]
+    sets = []
+    for _ in range(n_sets):
+        q, k, v = (x.clone() for x in base)
+        y = torch.empty_like(q)
+        ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
+        sets.append((q, k, v, y, torch.empty_like(q)))
+    del base
+    torch.cuda.synchronize()
+    for i in range(steps):
+        q, k, v, y, o = sets[i % n_sets]
+        if which == "stage_l":
+            ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
+        elif which == "stage_r":
+            ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
+        else:
+            o.copy_(q)
+    torch.cuda.synchronize()
+    print("profiled %s x%d" % (which, steps), flush=True)
+
+
 def main():
     args = parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, kernel=args.kernel)
+        return
+    if args.profile_only:
+        profile_only(args.profile_only, args.steps)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the method is measured on a single MI355X and "
               "this build has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
@@ -168,8 +258,8 @@ def main():
     achieved = (f / (dur * 1e-6) / 1e12) if mfma_bound else (b / (dur * 1e-6) / 1e9)
     peak = PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as fh:
+    if os.path.exists(TRAFFIC_FILE % name):
+        with open(TRAFFIC_FILE % name) as fh:
             tr = json.load(fh)
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("kernel") == name:
             traffic = tr.get("bytes_per_launch")

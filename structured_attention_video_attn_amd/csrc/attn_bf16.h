@@ -1,22 +1,33 @@
 // attn_bf16.h -- bf16 group softmax attention on the gfx950 matrix cores.
 //
-// One kernel serves stage R (blocks of contiguous tokens), stage L (stride-b2
-// token sets, untiled or cut into frame x row boxes) and dense attention: the
-// token groups come from a GroupAddr, so stage L gathers its rows straight
-// from the natural-order tensors and scatters its output to the same natural
-// positions; no permuted copy is written (MonarchRT summaries, nl
-// "Methodologie": a product of permutation and block-diagonal factors).
-// Like FlashAttention the score matrix never leaves the chip (zh 2.2: the
-// custom kernels keep the work in on-chip memory): each workgroup owns up to
-// 32*NW queries of one group and streams the group's keys and values through
-// LDS in tiles of 64 rows, keeping an online softmax.
+// Two kernels run softmax attention inside token groups described by a
+// GroupAddr, so stage L gathers its rows straight from the natural-order
+// tensors and scatters its output to the same natural positions; no permuted
+// copy is written (MonarchRT summaries, nl "Methodologie": a product of
+// permutation and block-diagonal factors). Like FlashAttention the score
+// matrix never leaves the chip (zh 2.2: the custom kernels keep the work in
+// on-chip memory).
+//
+//   group_attn_bf16  groups longer than 64 tokens (stage L, long stage-R
+//                    blocks, dense): a workgroup of 4 waves owns 128 queries
+//                    of one group and streams the group's keys and values
+//                    through LDS in 64-row tiles with an online softmax,
+//                    software-pipelined so that the S = QK^T products of
+//                    tile t+1 run on the matrix cores while the vector ALUs
+//                    do the softmax of tile t.
+//   block_attn_bf16  groups of at most 64 tokens (stage R's W-row blocks,
+//                    small tiles): persistent workgroups of 2 waves walk over
+//                    the groups and prefetch the next group's keys, values
+//                    and queries while computing the current one, keeping
+//                    HBM requests in flight at all times.
 //
 // Data movement. Key and value tiles go global -> LDS by direct-to-LDS DMA
 // (global_load_lds_dwordx4: lane l of an instruction fills LDS bytes
 // [16l, 16l+16) of that instruction's 1 KB window), row-major, 2*D bytes per
 // row, with the 16-byte chunks of row r permuted by an XOR swizzle so that
-// both read patterns below hit distinct LDS banks. With NBUF = 2 the DMA of
-// tile t+1 runs while tile t is computed; one barrier per tile.
+// both read patterns below hit distinct LDS banks. Every buffer is its own
+// LDS object, so the compiler can prove that a DMA in flight never aliases
+// the buffer being read and does not wait for it.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] B[16x32];
 // lane l holds A row l%32 and B column l%32, each with 8 k-slots 8*(l/32)+e;
@@ -34,10 +45,11 @@
 // point at four keys and one 4-column run give the receiving lanes one
 // head_dim column each across four keys.
 //
-// Softmax: exp2 with the scale s*log2(e) folded into one FMA per score; the
-// running max only moves (and the accumulator is only rescaled) when a tile's
-// max exceeds it by more than 8 (log2 units), so unnormalised weights stay
-// below 2^8 and the result is unchanged up to rounding.
+// Softmax: exp2 with the scale s*log2(e) folded into one FMA per score
+// (v_exp_f32 directly: weights that would be denormal are negligible); the
+// running max only moves (and the accumulator is only rescaled) when a
+// tile's max exceeds it by more than 8 (log2 units), so unnormalised weights
+// stay below 2^8 and the result is unchanged up to rounding.
 #pragma once
 #include "kernels_common.h"
 
@@ -45,6 +57,8 @@ namespace ma {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
@@ -53,7 +67,19 @@ typedef uint16_t u16;
 
 constexpr int kKeyTile = 64;       // keys per LDS tile
 constexpr int kQueriesPerWave = 32;
+constexpr int kBlockWaves = 2;     // waves per block_attn_bf16 workgroup
 constexpr float kLazyRescale = 8.f;
+
+template <int D>
+struct TileGeo {
+  static constexpr int DK = D / 16;              // k-steps of 16 over head_dim for S^T
+  static constexpr int DB = (D + 31) / 32;       // 32-row blocks of O^T
+  static constexpr int CPR = D / 8;              // 16-byte chunks per token row
+  static constexpr int ROWB = 2 * D;             // bytes per tile row
+  static constexpr int TILEB = kKeyTile * ROWB;  // bytes per tile
+  static constexpr int NINST = kKeyTile * CPR / 64;   // DMA instructions per tile
+  static constexpr int ROWS_PER_INST = 64 / CPR;
+};
 
 // Position of 16-byte chunk c of tile row r (CPR chunks per row, a power of 2).
 template <int CPR>
@@ -63,21 +89,214 @@ __device__ __forceinline__ int swizzle_chunk(int r, int c) {
   return c ^ s;
 }
 
-template <int D, int NW, int NBUF>
-__global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
-  constexpr int NT = NW * 64;
-  constexpr int DK = D / 16;              // k-steps of 16 over head_dim for S^T
-  constexpr int DB = (D + 31) / 32;       // 32-row blocks of O^T
-  constexpr int CPR = D / 8;              // 16-byte chunks per token row
-  constexpr int ROWB = 2 * D;             // bytes per tile row
-  constexpr int TILEB = kKeyTile * ROWB;  // bytes per tile and tensor
-  constexpr int NINST = kKeyTile * CPR / 64;   // DMA instructions per tile and tensor
+__device__ __forceinline__ float swap_halves(float x) {   // value of lane l ^ 32
+  auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
+}
 
-  // Two distinct LDS objects (not one array indexed by t % 2), so that the
-  // compiler can prove the DMA into one buffer never aliases reads of the
-  // other and does not wait for the prefetch before computing.
-  __shared__ __align__(1024) unsigned char smem0[2 * TILEB];
-  __shared__ __align__(1024) unsigned char smem1[NBUF > 1 ? 2 * TILEB : 16];
+// DMA of group rows [k0, k0 + 64) of one tensor into an LDS tile (waves of the
+// workgroup split the 1 KB windows). kSkipPast: windows wholly past the group
+// are skipped (their rows must already hold finite data); otherwise rows past
+// the group repeat its last member. Either way those rows are masked later.
+template <int D, bool kSkipPast>
+__device__ __forceinline__ void dma_tile(const unsigned char *src, unsigned char *dst,
+                                         const GroupGeom &geo, int32_t k0, int wave, int lane, int nw) {
+  using G = TileGeo<D>;
+  for (int ii = wave; ii < G::NINST; ii += nw) {
+    if (kSkipPast && k0 + ii * G::ROWS_PER_INST >= geo.len) break;   // wave-uniform
+    const int slot = ii * 64 + lane;
+    const int r = slot / G::CPR, pos = slot % G::CPR;
+    const int c = swizzle_chunk<G::CPR>(r, pos);
+    const int32_t km = min(k0 + r, geo.len - 1);
+    // offsets inside one (batch, head) slice fit in 32 bits (N * D < 2^31 elements)
+    const uint32_t off = ((uint32_t)member_token(geo, km) * D + c * 8) * 2u;
+    __builtin_amdgcn_global_load_lds((MA_GLOBAL void *)(src + off), (MA_LDS void *)(dst + ii * 1024), 16,
+                                     0, 0);
+  }
+}
+
+// This lane's query as the B operand of S^T = K Q^T: head_dim slots
+// [D/2*half + 8j, +8) for k-step j.
+template <int D>
+__device__ __forceinline__ void load_query(const u16 *qh, const GroupGeom &geo, int32_t qm, int half,
+                                           bf16x8_t *qb) {
+  const bool valid = qm < geo.len;
+  const u16 *qrow = qh + (uint32_t)(valid ? member_token(geo, qm) : 0) * D + (D / 2) * half;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const uint4 x = valid ? *reinterpret_cast<const uint4 *>(qrow + 8 * j) : make_uint4(0, 0, 0, 0);
+    qb[j] = __builtin_bit_cast(bf16x8_t, x);
+  }
+}
+
+// S^T for 32-key block kb of an LDS key tile (key operands fetched in
+// batches of 4 k-steps to bound register pressure).
+template <int D>
+__device__ __forceinline__ f32x16_t qk_block(const unsigned char *ks, const bf16x8_t *qb, int kb, int col,
+                                             int half) {
+  using G = TileGeo<D>;
+  constexpr int B = G::DK < 4 ? G::DK : 4;
+  const int r = 32 * kb + col;
+  f32x16_t acc = {};
+#pragma unroll
+  for (int j0 = 0; j0 < G::DK; j0 += B) {
+    bf16x8_t a[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      a[j] = *reinterpret_cast<const bf16x8_t *>(
+          ks + r * G::ROWB + 16 * swizzle_chunk<G::CPR>(r, (D / 16) * half + j0 + j));
+#pragma unroll
+    for (int j = 0; j < B; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], qb[j0 + j], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Online-softmax update for one 32-key block of scores (keys k0.. of a group
+// of len): mask, running max (lazy), exp2, running sum; returns P^T as the
+// B operands of the block's two PV steps.
+template <int DB>
+__device__ __forceinline__ void softmax_block(f32x16_t &s, int32_t k0, int32_t len, int half,
+                                              float scale_log2, float &m_run, float &l_run,
+                                              f32x16_t *oacc, bf16x8_t (&pb)[2]) {
+  if (k0 + 32 > len) {   // ragged block: keys past the group get -inf
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t key = k0 + 8 * (r / 4) + 4 * half + (r % 4);
+      if (key >= len) s[r] = -INFINITY;
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = fmaxf(mx, swap_halves(mx));   // the other 16 keys of this query
+  const float tmax = mx * scale_log2;
+  if (__any(tmax > m_run + kLazyRescale)) {
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    m_run = m_new;
+  }
+  float lsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], scale_log2, -m_run));
+    lsum += e0 + e1;
+    const bf16x2_t pr = __builtin_convertvector((f32x2_t){e0, e1}, bf16x2_t);   // v_cvt_pk_bf16_f32
+    pb[r / 8][r % 8] = pr[0];
+    pb[r / 8][r % 8 + 1] = pr[1];
+  }
+  l_run += lsum;
+}
+
+// O^T += Y^T P^T for 32-key block kb of an LDS value tile. Step h covers keys
+// 32kb+16h+[0,16); k-slot e of lane half `half` is key 32kb + 16h + 8(e/4) +
+// 4half + e%4, the key that S^T element r = 8h + e of this lane holds.
+template <int D>
+__device__ __forceinline__ void pv_block(const unsigned char *vs, const bf16x8_t (&pb)[2], int kb,
+                                         f32x16_t *oacc, int tr_key, int tr_col) {
+  using G = TileGeo<D>;
+#pragma unroll
+  for (int b = 0; b < G::DB; ++b) {
+    // head_dim column of this lane's source run; past head_dim (D = 16 only)
+    // the whole 16-lane group reads column 0 and feeds zero rows instead.
+    const int cidx = 32 * b + tr_col;
+    const bool dvalid = (G::DB * 32 == D) || cidx < D;
+    const int cc = dvalid ? cidx : 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r0 = 32 * kb + 16 * h + tr_key;
+      const int r1 = r0 + 8;
+      const unsigned char *p0 = vs + r0 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r0, cc >> 3) + 2 * (cc & 7);
+      const unsigned char *p1 = vs + r1 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r1, cc >> 3) + 2 * (cc & 7);
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)p0);
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)p1);
+      bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      if (!dvalid) a = bf16x8_t{};
+      oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h], oacc[b], 0, 0, 0);
+    }
+  }
+}
+
+// One 64-key tile: QK(block 1) is issued before the softmax of block 0 and
+// PV(block 0) before the softmax of block 1, so matrix-core work is in
+// flight while the vector ALUs run each softmax.
+template <int D>
+__device__ __forceinline__ void attend_tile(const unsigned char *ks, const unsigned char *vs,
+                                            const bf16x8_t *qb, int32_t k0, int32_t len, float scale_log2,
+                                            float &m_run, float &l_run, f32x16_t *oacc, int col, int half,
+                                            int tr_key, int tr_col) {
+  constexpr int DB = TileGeo<D>::DB;
+  f32x16_t s0 = qk_block<D>(ks, qb, 0, col, half);
+  f32x16_t s1 = qk_block<D>(ks, qb, 1, col, half);
+  bf16x8_t pb[2];
+  softmax_block<DB>(s0, k0, len, half, scale_log2, m_run, l_run, oacc, pb);
+  pv_block<D>(vs, pb, 0, oacc, tr_key, tr_col);
+  softmax_block<DB>(s1, k0 + 32, len, half, scale_log2, m_run, l_run, oacc, pb);
+  pv_block<D>(vs, pb, 1, oacc, tr_key, tr_col);
+}
+
+// Normalise and store this lane's query row (O^T element r of d-block b is
+// head_dim 32b + 8(r/4) + 4half + r%4).
+template <int D>
+__device__ __forceinline__ void store_row(u16 *orow, const f32x16_t *oacc, float l_run, int half) {
+  const float inv = 1.f / (l_run + swap_halves(l_run));
+#pragma unroll
+  for (int b = 0; b < TileGeo<D>::DB; ++b)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * b + 8 * rq + 4 * half;
+      if (d0 < D) {
+        bf16x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[b][4 * rq + e] * inv);
+        *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
+      }
+    }
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Streaming kernel for groups longer than one key tile.
+//
+// A workgroup of NW waves owns up to 32*NW queries of one group (p.q_tile of
+// them; waves whose queries all lie past that share skip the math but still
+// take part in the DMA and the barriers). Every wave reads the workgroup's
+// shared key/value tiles, so wide workgroups mean few L2 -> LDS copies of a
+// group's keys and values. Tiles go through a ring of NB LDS buffer pairs:
+// tile t lives in buffer t % NB and its DMA is issued NB-1 tiles ahead, at
+// the barrier that opens tile t-NB+1 (which frees the buffer tile t-NB used).
+// Vector-memory loads retire in order, so before tile t a wave waits only
+// until at most (tiles issued after t) x (its DMA instructions per tile) are
+// still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D, int NW, int NB>
+__global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
+  using G = TileGeo<D>;
+  static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
+  static_assert(NB >= 2 && NB <= 4, "ring of 2..4 buffers");
+  constexpr int PD = NB - 1;                     // tiles in flight ahead of the one computed
+  constexpr int PER_TILE = 2 * G::NINST / NW;    // DMA instructions per tile and wave (K and Y)
+  __shared__ __align__(1024) unsigned char kt0[G::TILEB];
+  __shared__ __align__(1024) unsigned char kt1[G::TILEB];
+  __shared__ __align__(1024) unsigned char kt2[NB > 2 ? G::TILEB : 16];
+  __shared__ __align__(1024) unsigned char kt3[NB > 3 ? G::TILEB : 16];
+  __shared__ __align__(1024) unsigned char yt0[G::TILEB];
+  __shared__ __align__(1024) unsigned char yt1[G::TILEB];
+  __shared__ __align__(1024) unsigned char yt2[NB > 2 ? G::TILEB : 16];
+  __shared__ __align__(1024) unsigned char yt3[NB > 3 ? G::TILEB : 16];
+  auto kbuf = [&](int j) -> unsigned char * { return j == 0 ? kt0 : j == 1 ? kt1 : j == 2 ? kt2 : kt3; };
+  auto ybuf = [&](int j) -> unsigned char * { return j == 0 ? yt0 : j == 1 ? yt1 : j == 2 ? yt2 : yt3; };
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
@@ -85,193 +304,157 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int32_t g = (int32_t)(rest % (uint32_t)p.ga.n_groups);
   const int64_t bh = (int64_t)(rest / (uint32_t)p.ga.n_groups);
   const GroupGeom geo = group_geom(p.ga, g);
-  if (qt * (kQueriesPerWave * NW) >= geo.len) return;   // uniform over the workgroup
+  const int32_t qbase = qt * p.q_tile;
+  if (qbase >= geo.len) return;   // uniform over the workgroup
+  const int32_t qend = min(geo.len, qbase + p.q_tile);
 
   const u16 *qh = static_cast<const u16 *>(p.q) + bh * p.head_elems;
-  const u16 *kh = static_cast<const u16 *>(p.k) + bh * p.head_elems;
-  const u16 *vh = static_cast<const u16 *>(p.vals) + bh * p.head_elems;
+  const unsigned char *kbytes =
+      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + bh * p.head_elems);
+  const unsigned char *vbytes =
+      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + bh * p.head_elems);
   u16 *oh = static_cast<u16 *>(p.out) + bh * p.head_elems;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
+  const int tr_key = 4 * half + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // DMA of one key tile and its value tile into buffer `buf`. Rows past the
-  // group repeat its last member: finite data whose scores are masked to -inf.
-  auto issue_tile = [&](int32_t k0, unsigned char *kb_lds) {
-    unsigned char *vb_lds = kb_lds + TILEB;
-#pragma unroll
-    for (int ii = wave; ii < NINST; ii += NW) {
-      const int slot = ii * 64 + lane;
-      const int r = slot / CPR, pos = slot % CPR;
-      const int c = swizzle_chunk<CPR>(r, pos);
-      const int32_t km = min(k0 + r, geo.len - 1);
-      const int64_t off = (int64_t)member_token(geo, km) * D + c * 8;
-      __builtin_amdgcn_global_load_lds((MA_GLOBAL void *)(kh + off), (MA_LDS void *)(kb_lds + ii * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((MA_GLOBAL void *)(vh + off), (MA_LDS void *)(vb_lds + ii * 1024),
-                                       16, 0, 0);
-    }
+  const int32_t q0 = qbase + wave * kQueriesPerWave;
+  const int32_t qm = q0 + col;
+  const bool wave_active = q0 < qend;   // wave-uniform
+  GroupGeom qgeo = geo;
+  qgeo.len = qend;                       // queries past this workgroup's share load zeros
+  bf16x8_t qb[G::DK];
+  load_query<D>(qh, qgeo, qm, half, qb);
+
+  // (queries were requested first, so the first tile's wait also covers them)
+  const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
+  auto issue = [&](int32_t t, int j) {
+    dma_tile<D, false>(kbytes, kbuf(j), geo, t * kKeyTile, wave, lane, NW);
+    dma_tile<D, false>(vbytes, ybuf(j), geo, t * kKeyTile, wave, lane, NW);
   };
-
-  const int32_t ntiles = (geo.len + kKeyTile - 1) / kKeyTile;
-  issue_tile(0, smem0);
-
-  // This lane's query (column of S^T), head_dim slots [D/2*half, D/2*half + D/2).
-  const int32_t qm = qt * (kQueriesPerWave * NW) + wave * kQueriesPerWave + col;
-  const bool qvalid = qm < geo.len;
-  const int32_t qtok = qvalid ? member_token(geo, qm) : 0;
-  bf16x8_t qb[DK];
-  {
-    const u16 *qrow = qh + (int64_t)qtok * D + (D / 2) * half;
 #pragma unroll
-    for (int j = 0; j < DK; ++j) {
-      uint4 x = qvalid ? *reinterpret_cast<const uint4 *>(qrow + 8 * j) : make_uint4(0, 0, 0, 0);
-      qb[j] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
+  for (int j = 0; j < PD; ++j)
+    if (j < n) issue(j, j);
 
-  f32x16_t oacc[DB];
+  f32x16_t oacc[G::DB];
 #pragma unroll
-  for (int b = 0; b < DB; ++b) oacc[b] = f32x16_t{};
+  for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Transposed-read source coordinates of this lane (see the header comment).
-  const int tr_grp = lane >> 4, tr_i = lane & 15;
-  const int tr_key = 4 * half + (tr_i >> 2);                        // + 32kb + 16h (+8)
-  const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_i & 3);           // + 32b
-
-  auto compute_tile = [&](int32_t k0, const unsigned char *ks) {
-    const unsigned char *vs = ks + TILEB;
-    // S^T for the two 32-key blocks of this tile.
-    f32x16_t s[2];
+  for (int32_t t0 = 0; t0 < n; t0 += NB) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      const int r = 32 * kb + col;
-      bf16x8_t a[DK];
-#pragma unroll
-      for (int j = 0; j < DK; ++j)
-        a[j] = *reinterpret_cast<const bf16x8_t *>(
-            ks + r * ROWB + 16 * swizzle_chunk<CPR>(r, (D / 16) * half + j));
-#pragma unroll
-      for (int j = 0; j < DK; ++j)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], qb[j], s[kb], 0, 0, 0);
-    }
-    if (k0 + kKeyTile > geo.len) {   // ragged last tile: keys past the group get -inf
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t key = k0 + 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-          if (key >= geo.len) s[kb][r] = -INFINITY;
-        }
-    }
-
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));          // the other 32 keys of this query
-    const float tmax = mx * p.scale_log2;
-    if (__any(tmax > m_run + kLazyRescale)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-      m_run = m_new;
-    }
-
-    bf16x8_t pb[2][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(fmaf(s[kb][r], p.scale_log2, -m_run));
-        lsum += e;
-        pb[kb][r / 8][r % 8] = (__bf16)e;
-      }
-    l_run += lsum;
-
-    // O^T += Y^T P^T. Step (kb, h) covers keys 32kb+16h+[0,16); k-slot e of
-    // lane half `half` is key 32kb + 16h + 8(e/4) + 4half + e%4, the key that
-    // S^T element r = 8h + e of this lane holds.
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      // head_dim column of this lane's source run; past head_dim (D = 16 only)
-      // the whole 16-lane group reads column 0 and feeds zero rows instead.
-      const int cidx = 32 * b + tr_col;
-      const bool dvalid = (DB * 32 == D) || cidx < D;
-      const int cc = dvalid ? cidx : 0;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r0 = 32 * kb + 16 * h + tr_key;
-          const int r1 = r0 + 8;
-          const unsigned char *p0 =
-              vs + r0 * ROWB + 16 * swizzle_chunk<CPR>(r0, cc >> 3) + 2 * (cc & 7);
-          const unsigned char *p1 =
-              vs + r1 * ROWB + 16 * swizzle_chunk<CPR>(r1, cc >> 3) + 2 * (cc & 7);
-          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)p0);
-          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)p1);
-          bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          if (!dvalid) a = bf16x8_t{};
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][h], oacc[b], 0, 0, 0);
-        }
-    }
-  };
-
-  // Tile t lives in smem0 for even t and in smem1 for odd t (NBUF = 2); the
-  // DMA of tile t+1 is issued right after the barrier that opens tile t.
-  for (int32_t t = 0; t < ntiles; t += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if constexpr (NBUF > 1) {
-      if (t + 1 < ntiles) issue_tile((t + 1) * kKeyTile, smem1);
-    }
-    compute_tile(t * kKeyTile, smem0);
-    if (t + 1 >= ntiles) break;
-    if constexpr (NBUF > 1) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (t + 2 < ntiles) issue_tile((t + 2) * kKeyTile, smem0);
-      compute_tile((t + 1) * kKeyTile, smem1);
-    } else {   // single buffer: refill only after every wave is done with it
-      __syncthreads();
-      issue_tile((t + 1) * kKeyTile, smem0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      compute_tile((t + 1) * kKeyTile, smem0);
-      if (t + 2 < ntiles) {
-        __syncthreads();
-        issue_tile((t + 2) * kKeyTile, smem0);
-      }
+    for (int j = 0; j < NB; ++j) {
+      const int32_t t = t0 + j;
+      if (t >= n) break;
+      const int32_t after = min(PD - 1, n - 1 - t);   // tiles issued after t, maybe in flight
+      if (after <= 0) wait_vmcnt<0>();
+      else if (after == 1) wait_vmcnt<PER_TILE>();
+      else wait_vmcnt<2 * PER_TILE>();
+      __syncthreads();   // tile t visible to all waves; buffer (j + PD) % NB no longer read
+      if (t + PD < n) issue(t + PD, (j + PD) % NB);
+      if (wave_active)
+        attend_tile<D>(kbuf(j), ybuf(j), qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col,
+                       half, tr_key, tr_col);
     }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qvalid) {
-    const float inv = 1.f / l_tot;
-    u16 *orow = oh + (int64_t)qtok * D;
+  if (qm < qend) store_row<D>(oh + (uint32_t)member_token(geo, qm) * D, oacc, l_run, half);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent kernel for groups of at most 64 tokens. Workgroup w handles items
+// w, w + G, w + 2G, ... (item = group + n_groups * (batch*head)); the keys and
+// values of item i+G go into the other LDS buffer pair, and its queries into
+// registers, while item i is computed. A wave waits for that prefetch only
+// right before its output stores, when it has had a whole item's compute to
+// land; the barrier opening the next item then publishes it to both waves.
+template <int D>
+__global__ __launch_bounds__(kBlockWaves * 64, 2) void block_attn_bf16(AttnLaunch p, int32_t n_items) {
+  using G = TileGeo<D>;
+  constexpr int NW = kBlockWaves;
+  __shared__ __align__(1024) unsigned char kt0[G::TILEB];
+  __shared__ __align__(1024) unsigned char kt1[G::TILEB];
+  __shared__ __align__(1024) unsigned char yt0[G::TILEB];
+  __shared__ __align__(1024) unsigned char yt1[G::TILEB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int tr_key = 4 * half + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // Rows past a group are never loaded; start from finite (zero) tiles.
+  for (int i = threadIdx.x; i < G::TILEB / 16; i += NW * 64) {
+    reinterpret_cast<uint4 *>(kt0)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4 *>(kt1)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4 *>(yt0)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4 *>(yt1)[i] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  int32_t item = blockIdx.x;
+  if (item >= n_items) return;   // uniform
+  const int32_t stride = gridDim.x;
+
+  struct Item {
+    GroupGeom geo;
+    int64_t bh;
+  };
+  auto decode = [&](int32_t it) {
+    Item r;
+    r.geo = group_geom(p.ga, it % p.ga.n_groups);
+    r.bh = it / p.ga.n_groups;
+    return r;
+  };
+  auto issue = [&](const Item &it, unsigned char *kd, unsigned char *yd, bf16x8_t *qdst) {
+    const unsigned char *kb =
+        reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + it.bh * p.head_elems);
+    const unsigned char *vb =
+        reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + it.bh * p.head_elems);
+    dma_tile<D, true>(kb, kd, it.geo, 0, wave, lane, NW);
+    dma_tile<D, true>(vb, yd, it.geo, 0, wave, lane, NW);
+    load_query<D>(static_cast<const u16 *>(p.q) + it.bh * p.head_elems, it.geo,
+                  wave * kQueriesPerWave + col, half, qdst);
+  };
+
+  Item cur = decode(item);
+  bf16x8_t qb[G::DK], qn[G::DK];
+  issue(cur, kt0, yt0, qb);
+  wait_dma();
+
+  auto phase = [&](const unsigned char *kc, const unsigned char *yc, unsigned char *kn, unsigned char *yn) {
+    __syncthreads();   // the item's tiles are visible to both waves; kn/yn are no longer read
+    const int32_t nxt = item + stride;
+    Item next = cur;
+    if (nxt < n_items) {
+      next = decode(nxt);
+      issue(next, kn, yn, qn);
+    }
+    f32x16_t oacc[G::DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.f;
+    attend_tile<D>(kc, yc, qb, 0, cur.geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key, tr_col);
+    const int32_t qm = wave * kQueriesPerWave + col;
+    wait_dma();   // the prefetch of `next` (and older stores) completed
+    if (qm < cur.geo.len) {
+      u16 *oh = static_cast<u16 *>(p.out) + cur.bh * p.head_elems;
+      store_row<D>(oh + (uint32_t)member_token(cur.geo, qm) * D, oacc, l_run, half);
+    }
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = 32 * b + 8 * rq + 4 * half;
-        if (d0 < D) {
-          bf16x4_t v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[b][4 * rq + e] * inv);
-          *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
-        }
-      }
+    for (int j = 0; j < G::DK; ++j) qb[j] = qn[j];
+    cur = next;
+    item = nxt;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  while (true) {
+    phase(kt0, yt0, kt1, yt1);
+    if (item >= n_items) break;
+    phase(kt1, yt1, kt0, yt0);
+    if (item >= n_items) break;
   }
 }
 

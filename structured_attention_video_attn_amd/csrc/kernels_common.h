@@ -17,6 +17,7 @@ struct AttnLaunch {
   int64_t head_elems; // N * head_dim: distance between consecutive (batch, head) slices
   GroupAddr ga;
   int32_t n_qtiles;   // query tiles per group (sized for the largest group)
+  int32_t q_tile;     // queries per query tile (streaming bf16 kernel)
   int32_t n_bh;       // batch * heads
   float scale;        // 1/sqrt(head_dim)
   float scale_log2;   // scale * log2(e): softmax evaluated with exp2

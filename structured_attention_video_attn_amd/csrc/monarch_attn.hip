@@ -11,6 +11,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/monarch_attn.h"
 #include "attn_bf16.h"
 #include "attn_f32.h"
@@ -27,24 +29,74 @@ int hip_status(hipError_t e) {
   return MA_ERR_HIP;
 }
 
+enum class Kernel { kF32, kBlock, kStream };
+
+// Host-side plan of one group-attention launch.
+struct Plan {
+  AttnLaunch a;
+  uint32_t blocks;    // workgroups (the persistent kernel: an upper bound, see run_plan)
+  int32_t n_items;    // groups * batch * heads (persistent kernel only)
+  int32_t waves;      // waves per workgroup (streaming kernel only)
+  Kernel kernel;
+};
+
+// Compute units of the current device, cached per device (the persistent
+// kernel launches two resident workgroups per CU).
+int device_cus(int *cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return MA_OK;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (c <= 0) c = 1;
+  if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return MA_OK;
+}
+
 template <int D>
-int launch_d(const AttnLaunch &a, int nw, uint32_t blocks, hipStream_t s) {
-  if (nw == 0) {
-    hipLaunchKernelGGL(group_attn_f32<D>, dim3(blocks), dim3(kF32Threads), 0, s, a);
-  } else if (nw == 2) {   // groups of at most 64 tokens: one key tile
-    hipLaunchKernelGGL((group_attn_bf16<D, 2, 1>), dim3(blocks), dim3(128), 0, s, a);
-  } else {                 // longer groups: double-buffered key/value tiles
-    hipLaunchKernelGGL((group_attn_bf16<D, 4, 2>), dim3(blocks), dim3(256), 0, s, a);
+int launch_d(const Plan &pl, hipStream_t s) {
+  switch (pl.kernel) {
+    case Kernel::kF32:
+      hipLaunchKernelGGL(group_attn_f32<D>, dim3(pl.blocks), dim3(kF32Threads), 0, s, pl.a);
+      break;
+    case Kernel::kBlock: {
+      int cus = 0;
+      const int st = device_cus(&cus);
+      if (st != MA_OK) return st;
+      const uint32_t resident = 2u * (uint32_t)cus;
+      const uint32_t blocks = pl.blocks < resident ? pl.blocks : resident;
+      hipLaunchKernelGGL(block_attn_bf16<D>, dim3(blocks), dim3(kBlockWaves * 64), 0, s, pl.a, pl.n_items);
+      break;
+    }
+    default:
+      // waves per workgroup; every wave must issue whole DMA instructions
+      if constexpr (TileGeo<D>::NINST % 8 == 0) {
+        if (pl.waves >= 8) {
+          hipLaunchKernelGGL((group_attn_bf16<D, 8, 4>), dim3(pl.blocks), dim3(8 * 64), 0, s, pl.a);
+          break;
+        }
+      }
+      if constexpr (TileGeo<D>::NINST % 4 == 0) {
+        if (pl.waves >= 4) {
+          hipLaunchKernelGGL((group_attn_bf16<D, 4, 2>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((group_attn_bf16<D, 2, 2>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
+      break;
   }
   return hip_status(hipGetLastError());
 }
-
-// Host-side plan of one group-attention launch; fails before any HIP call.
-struct Plan {
-  AttnLaunch a;
-  uint32_t blocks;
-  int nw;   // waves per workgroup of the chosen kernel (0: fp32 kernel)
-};
 
 int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void *k,
                 const void *vals, void *out, Plan *pl) {
@@ -61,15 +113,35 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
   int q_per_block;
   if (p.dtype == MA_F32) {
     q_per_block = kF32Threads;
-    pl->nw = 0;
+    pl->kernel = Kernel::kF32;
+  } else if (ga.max_len <= kKeyTile) {
+    q_per_block = kKeyTile;   // one group per work item
+    pl->kernel = Kernel::kBlock;
   } else {
-    pl->nw = ga.max_len <= kQueriesPerWave * 2 ? 2 : 4;
-    q_per_block = kQueriesPerWave * pl->nw;
+    // Workgroups of up to 4 waves (128 queries), two resident per CU with a
+    // double-buffered ring: measured faster on MI355X than 8-wave workgroups
+    // with a 4-deep ring, whose waves all meet at every barrier together even
+    // though they copy each group's keys and values into LDS fewer times.
+    // The group's queries are spread evenly over its workgroups; the wave
+    // count is the power of two that covers a share and that the DMA split
+    // allows (D/8 16-byte chunks per row).
+    const int max_waves = p.D >= 32 ? 4 : 2;
+    const int64_t cap = (int64_t)kQueriesPerWave * max_waves;
+    const int64_t per_group = (ga.max_len + cap - 1) / cap;
+    const int64_t share = (ga.max_len + per_group - 1) / per_group;
+    const int64_t need = (share + kQueriesPerWave - 1) / kQueriesPerWave;
+    int w = 2;
+    while (w < need && w < max_waves) w *= 2;
+    pl->waves = w;
+    q_per_block = (int)(kQueriesPerWave * need);
+    pl->kernel = Kernel::kStream;
   }
   a.n_qtiles = (ga.max_len + q_per_block - 1) / q_per_block;
+  a.q_tile = q_per_block;
   const uint64_t blocks = (uint64_t)a.n_qtiles * (uint64_t)ga.n_groups * (uint64_t)a.n_bh;
   if (blocks > (uint64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
   pl->blocks = (uint32_t)blocks;
+  pl->n_items = (int32_t)blocks;
   pl->a = a;
   return MA_OK;
 }
@@ -77,10 +149,10 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
 int run_plan(const Problem &p, const Plan &pl, hipStream_t s) {
   if (pl.blocks == 0) return MA_OK;
   switch (p.D) {
-    case 16: return launch_d<16>(pl.a, pl.nw, pl.blocks, s);
-    case 32: return launch_d<32>(pl.a, pl.nw, pl.blocks, s);
-    case 64: return launch_d<64>(pl.a, pl.nw, pl.blocks, s);
-    default: return launch_d<128>(pl.a, pl.nw, pl.blocks, s);
+    case 16: return launch_d<16>(pl, s);
+    case 32: return launch_d<32>(pl, s);
+    case 64: return launch_d<64>(pl, s);
+    default: return launch_d<128>(pl, s);
   }
 }
 
