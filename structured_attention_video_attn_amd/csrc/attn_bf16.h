@@ -115,6 +115,19 @@ __device__ __forceinline__ void dma_tile(const unsigned char *src, unsigned char
   }
 }
 
+// One DMA instruction (1 KB window ii) of a tile; see dma_tile.
+template <int D>
+__device__ __forceinline__ void dma_window(const unsigned char *src, unsigned char *dst, const GroupGeom &geo,
+                                           int32_t k0, int ii, int lane) {
+  using G = TileGeo<D>;
+  const int slot = ii * 64 + lane;
+  const int r = slot / G::CPR, pos = slot % G::CPR;
+  const int c = swizzle_chunk<G::CPR>(r, pos);
+  const int32_t km = min(k0 + r, geo.len - 1);
+  const uint32_t off = ((uint32_t)member_token(geo, km) * D + c * 8) * 2u;
+  __builtin_amdgcn_global_load_lds((MA_GLOBAL void *)(src + off), (MA_LDS void *)(dst + ii * 1024), 16, 0, 0);
+}
+
 // This lane's query as the B operand of S^T = K Q^T: head_dim slots
 // [D/2*half + 8j, +8) for k-step j.
 template <int D>
@@ -131,9 +144,9 @@ __device__ __forceinline__ void load_query(const u16 *qh, const GroupGeom &geo, 
 
 // S^T for 32-key block kb of an LDS key tile (key operands fetched in
 // batches of 4 k-steps to bound register pressure).
-template <int D>
+template <int D, typename Hook>
 __device__ __forceinline__ f32x16_t qk_block(const unsigned char *ks, const bf16x8_t *qb, int kb, int col,
-                                             int half) {
+                                             int half, Hook &&hook) {
   using G = TileGeo<D>;
   constexpr int B = G::DK < 4 ? G::DK : 4;
   const int r = 32 * kb + col;
@@ -147,6 +160,7 @@ __device__ __forceinline__ f32x16_t qk_block(const unsigned char *ks, const bf16
           ks + r * G::ROWB + 16 * swizzle_chunk<G::CPR>(r, (D / 16) * half + j0 + j));
 #pragma unroll
     for (int j = 0; j < B; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], qb[j0 + j], acc, 0, 0, 0);
+    hook(kb * (G::DK / B) + j0 / B);   // QK batch index across the two 32-key blocks
   }
   return acc;
 }
@@ -196,9 +210,9 @@ __device__ __forceinline__ void softmax_block(f32x16_t &s, int32_t k0, int32_t l
 // O^T += Y^T P^T for 32-key block kb of an LDS value tile. Step h covers keys
 // 32kb+16h+[0,16); k-slot e of lane half `half` is key 32kb + 16h + 8(e/4) +
 // 4half + e%4, the key that S^T element r = 8h + e of this lane holds.
-template <int D>
+template <int D, typename Hook>
 __device__ __forceinline__ void pv_block(const unsigned char *vs, const bf16x8_t (&pb)[2], int kb,
-                                         f32x16_t *oacc, int tr_key, int tr_col) {
+                                         f32x16_t *oacc, int tr_key, int tr_col, Hook &&hook) {
   using G = TileGeo<D>;
 #pragma unroll
   for (int b = 0; b < G::DB; ++b) {
@@ -219,25 +233,38 @@ __device__ __forceinline__ void pv_block(const unsigned char *vs, const bf16x8_t
       if (!dvalid) a = bf16x8_t{};
       oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h], oacc[b], 0, 0, 0);
     }
+    hook(G::DB * kb + b);   // d-block index across the two 32-key blocks
   }
 }
 
 // One 64-key tile: QK(block 1) is issued before the softmax of block 0 and
 // PV(block 0) before the softmax of block 1, so matrix-core work is in
-// flight while the vector ALUs run each softmax.
+// flight while the vector ALUs run each softmax. `on_qk(i)` runs after each
+// batch of QK MFMAs and `on_pv(i)` after each PV d-block; the streaming
+// kernel issues its next DMA instructions there one at a time, so that no
+// wave stalls behind a burst of its own memory instructions.
+template <int D, typename FQ, typename FP>
+__device__ __forceinline__ void attend_tile(const unsigned char *ks, const unsigned char *vs,
+                                            const bf16x8_t *qb, int32_t k0, int32_t len, float scale_log2,
+                                            float &m_run, float &l_run, f32x16_t *oacc, int col, int half,
+                                            int tr_key, int tr_col, FQ &&on_qk, FP &&on_pv) {
+  constexpr int DB = TileGeo<D>::DB;
+  f32x16_t s0 = qk_block<D>(ks, qb, 0, col, half, on_qk);
+  f32x16_t s1 = qk_block<D>(ks, qb, 1, col, half, on_qk);
+  bf16x8_t pb[2];
+  softmax_block<DB>(s0, k0, len, half, scale_log2, m_run, l_run, oacc, pb);
+  pv_block<D>(vs, pb, 0, oacc, tr_key, tr_col, on_pv);
+  softmax_block<DB>(s1, k0 + 32, len, half, scale_log2, m_run, l_run, oacc, pb);
+  pv_block<D>(vs, pb, 1, oacc, tr_key, tr_col, on_pv);
+}
+
 template <int D>
 __device__ __forceinline__ void attend_tile(const unsigned char *ks, const unsigned char *vs,
                                             const bf16x8_t *qb, int32_t k0, int32_t len, float scale_log2,
                                             float &m_run, float &l_run, f32x16_t *oacc, int col, int half,
                                             int tr_key, int tr_col) {
-  constexpr int DB = TileGeo<D>::DB;
-  f32x16_t s0 = qk_block<D>(ks, qb, 0, col, half);
-  f32x16_t s1 = qk_block<D>(ks, qb, 1, col, half);
-  bf16x8_t pb[2];
-  softmax_block<DB>(s0, k0, len, half, scale_log2, m_run, l_run, oacc, pb);
-  pv_block<D>(vs, pb, 0, oacc, tr_key, tr_col);
-  softmax_block<DB>(s1, k0 + 32, len, half, scale_log2, m_run, l_run, oacc, pb);
-  pv_block<D>(vs, pb, 1, oacc, tr_key, tr_col);
+  attend_tile<D>(ks, vs, qb, k0, len, scale_log2, m_run, l_run, oacc, col, half, tr_key, tr_col,
+                 [](int) {}, [](int) {});
 }
 
 // Normalise and store this lane's query row (O^T element r of d-block b is
@@ -354,10 +381,33 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
       else if (after == 1) wait_vmcnt<PER_TILE>();
       else wait_vmcnt<2 * PER_TILE>();
       __syncthreads();   // tile t visible to all waves; buffer (j + PD) % NB no longer read
-      if (t + PD < n) issue(t + PD, (j + PD) % NB);
-      if (wave_active)
+      const bool more = t + PD < n;
+      const int jn = (j + PD) % NB;
+      const int32_t kn0 = (t + PD) * kKeyTile;
+      // This wave's DMA windows are wave, wave + NW, ...: WPT of them per
+      // tensor, spread evenly over the QK batches (keys) and the PV d-blocks
+      // (values); any left over go out after the tile.
+      constexpr int WPT = G::NINST / NW;
+      constexpr int NQ = 2 * (G::DK < 4 ? 1 : G::DK / 4);   // QK hook points per tile
+      constexpr int NP = 2 * G::DB;                          // PV hook points per tile
+      constexpr int SQ = NQ >= WPT ? NQ / WPT : 1, SP = NP >= WPT ? NP / WPT : 1;
+      auto on_qk = [&](int i) {
+        if (more && i % SQ == 0 && i / SQ < WPT) dma_window<D>(kbytes, kbuf(jn), geo, kn0, wave + NW * (i / SQ), lane);
+      };
+      auto on_pv = [&](int i) {
+        if (more && i % SP == 0 && i / SP < WPT) dma_window<D>(vbytes, ybuf(jn), geo, kn0, wave + NW * (i / SP), lane);
+      };
+      if (wave_active) {
         attend_tile<D>(kbuf(j), ybuf(j), qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col,
-                       half, tr_key, tr_col);
+                       half, tr_key, tr_col, on_qk, on_pv);
+        if (more) {   // windows left over when there are fewer hook points than windows
+          for (int w = NQ / SQ; w < WPT; ++w) dma_window<D>(kbytes, kbuf(jn), geo, kn0, wave + NW * w, lane);
+          for (int w = NP / SP; w < WPT; ++w) dma_window<D>(vbytes, ybuf(jn), geo, kn0, wave + NW * w, lane);
+        }
+      } else if (more) {
+        dma_tile<D, false>(kbytes, kbuf(jn), geo, kn0, wave, lane, NW);
+        dma_tile<D, false>(vbytes, ybuf(jn), geo, kn0, wave, lane, NW);
+      }
     }
   }
 

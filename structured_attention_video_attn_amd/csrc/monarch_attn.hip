@@ -80,12 +80,6 @@ int launch_d(const Plan &pl, hipStream_t s) {
     }
     default:
       // waves per workgroup; every wave must issue whole DMA instructions
-      if constexpr (TileGeo<D>::NINST % 8 == 0) {
-        if (pl.waves >= 8) {
-          hipLaunchKernelGGL((group_attn_bf16<D, 8, 4>), dim3(pl.blocks), dim3(8 * 64), 0, s, pl.a);
-          break;
-        }
-      }
       if constexpr (TileGeo<D>::NINST % 4 == 0) {
         if (pl.waves >= 4) {
           hipLaunchKernelGGL((group_attn_bf16<D, 4, 2>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
