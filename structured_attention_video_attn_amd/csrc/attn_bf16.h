@@ -142,27 +142,36 @@ __device__ __forceinline__ void load_query(const u16 *qh, const GroupGeom &geo, 
   }
 }
 
-// S^T for 32-key block kb of an LDS key tile (key operands fetched in
-// batches of 4 k-steps to bound register pressure).
+// S^T for both 32-key blocks of an LDS key tile. The two accumulators are
+// independent chains, interleaved so the matrix pipe never waits on a
+// result; key operands are fetched in batches of 4 k-steps per block to
+// bound register pressure. hook(i) runs after batch i (0 .. 2*DK/B - 1).
 template <int D, typename Hook>
-__device__ __forceinline__ f32x16_t qk_block(const unsigned char *ks, const bf16x8_t *qb, int kb, int col,
-                                             int half, Hook &&hook) {
+__device__ __forceinline__ void qk_tile(const unsigned char *ks, const bf16x8_t *qb, int col, int half,
+                                        f32x16_t &s0, f32x16_t &s1, Hook &&hook) {
   using G = TileGeo<D>;
   constexpr int B = G::DK < 4 ? G::DK : 4;
-  const int r = 32 * kb + col;
-  f32x16_t acc = {};
+  const int r0 = col, r1 = 32 + col;
+  f32x16_t a0 = {}, a1 = {};
 #pragma unroll
   for (int j0 = 0; j0 < G::DK; j0 += B) {
-    bf16x8_t a[B];
+    bf16x8_t k0[B], k1[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j)
-      a[j] = *reinterpret_cast<const bf16x8_t *>(
-          ks + r * G::ROWB + 16 * swizzle_chunk<G::CPR>(r, (D / 16) * half + j0 + j));
+    for (int j = 0; j < B; ++j) {
+      const int c = (D / 16) * half + j0 + j;
+      k0[j] = *reinterpret_cast<const bf16x8_t *>(ks + r0 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r0, c));
+      k1[j] = *reinterpret_cast<const bf16x8_t *>(ks + r1 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r1, c));
+    }
 #pragma unroll
-    for (int j = 0; j < B; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], qb[j0 + j], acc, 0, 0, 0);
-    hook(kb * (G::DK / B) + j0 / B);   // QK batch index across the two 32-key blocks
+    for (int j = 0; j < B; ++j) {
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[j], qb[j0 + j], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[j], qb[j0 + j], a1, 0, 0, 0);
+    }
+    hook(2 * (j0 / B));
+    hook(2 * (j0 / B) + 1);
   }
-  return acc;
+  s0 = a0;
+  s1 = a1;
 }
 
 // Online-softmax update for one 32-key block of scores (keys k0.. of a group
@@ -215,16 +224,16 @@ __device__ __forceinline__ void pv_block(const unsigned char *vs, const bf16x8_t
                                          f32x16_t *oacc, int tr_key, int tr_col, Hook &&hook) {
   using G = TileGeo<D>;
 #pragma unroll
-  for (int b = 0; b < G::DB; ++b) {
-    // head_dim column of this lane's source run; past head_dim (D = 16 only)
-    // the whole 16-lane group reads column 0 and feeds zero rows instead.
-    const int cidx = 32 * b + tr_col;
-    const bool dvalid = (G::DB * 32 == D) || cidx < D;
-    const int cc = dvalid ? cidx : 0;
+  for (int h = 0; h < 2; ++h) {   // k-step outer: the DB accumulators are independent chains
+    const int r0 = 32 * kb + 16 * h + tr_key;
+    const int r1 = r0 + 8;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r0 = 32 * kb + 16 * h + tr_key;
-      const int r1 = r0 + 8;
+    for (int b = 0; b < G::DB; ++b) {
+      // head_dim column of this lane's source run; past head_dim (D = 16 only)
+      // the whole 16-lane group reads column 0 and feeds zero rows instead.
+      const int cidx = 32 * b + tr_col;
+      const bool dvalid = (G::DB * 32 == D) || cidx < D;
+      const int cc = dvalid ? cidx : 0;
       const unsigned char *p0 = vs + r0 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r0, cc >> 3) + 2 * (cc & 7);
       const unsigned char *p1 = vs + r1 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r1, cc >> 3) + 2 * (cc & 7);
       const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)p0);
@@ -232,8 +241,8 @@ __device__ __forceinline__ void pv_block(const unsigned char *vs, const bf16x8_t
       bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       if (!dvalid) a = bf16x8_t{};
       oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[h], oacc[b], 0, 0, 0);
+      if (h == 1) hook(G::DB * kb + b);   // d-block index across the two 32-key blocks
     }
-    hook(G::DB * kb + b);   // d-block index across the two 32-key blocks
   }
 }
 
@@ -249,8 +258,8 @@ __device__ __forceinline__ void attend_tile(const unsigned char *ks, const unsig
                                             float &m_run, float &l_run, f32x16_t *oacc, int col, int half,
                                             int tr_key, int tr_col, FQ &&on_qk, FP &&on_pv) {
   constexpr int DB = TileGeo<D>::DB;
-  f32x16_t s0 = qk_block<D>(ks, qb, 0, col, half, on_qk);
-  f32x16_t s1 = qk_block<D>(ks, qb, 1, col, half, on_qk);
+  f32x16_t s0, s1;
+  qk_tile<D>(ks, qb, col, half, s0, s1, on_qk);
   bf16x8_t pb[2];
   softmax_block<DB>(s0, k0, len, half, scale_log2, m_run, l_run, oacc, pb);
   pv_block<D>(vs, pb, 0, oacc, tr_key, tr_col, on_pv);
@@ -294,36 +303,33 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // A workgroup of NW waves owns up to 32*NW queries of one group (p.q_tile of
 // them; waves whose queries all lie past that share skip the math but still
 // take part in the DMA and the barriers). Every wave reads the workgroup's
-// shared key/value tiles, so wide workgroups mean few L2 -> LDS copies of a
-// group's keys and values. Tiles go through a ring of NB LDS buffer pairs:
-// tile t lives in buffer t % NB and its DMA is issued NB-1 tiles ahead, at
-// the barrier that opens tile t-NB+1 (which frees the buffer tile t-NB used).
-// Vector-memory loads retire in order, so before tile t a wave waits only
-// until at most (tiles issued after t) x (its DMA instructions per tile) are
-// still in flight.
+// shared key/value tiles.
+//
+// Rings: key tiles in KB LDS buffers (tile t in buffer t % KB), value tiles in
+// two (t % 2). While computing tile t a wave issues the value windows of tile
+// t+1 right after its QK MFMA batches, and the key windows of tile t+KB-1
+// after its PV d-blocks, one DMA instruction at a time. The barrier opening
+// tile t+1 therefore waits only for DMAs issued about a tile earlier (values)
+// or two tiles earlier (keys, KB = 3). Vector-memory loads retire in order, so
+// the wait may leave the newest key windows in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int NW, int NB>
+template <int D, int NW, int KB>
 __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
-  static_assert(NB >= 2 && NB <= 4, "ring of 2..4 buffers");
-  constexpr int PD = NB - 1;                     // tiles in flight ahead of the one computed
-  constexpr int PER_TILE = 2 * G::NINST / NW;    // DMA instructions per tile and wave (K and Y)
+  static_assert(KB == 2 || KB == 3, "key ring of 2 or 3 buffers");
+  constexpr int PK = KB - 1;                 // key tiles issued ahead
+  constexpr int WPT = G::NINST / NW;         // DMA windows per tile, tensor and wave
   __shared__ __align__(1024) unsigned char kt0[G::TILEB];
   __shared__ __align__(1024) unsigned char kt1[G::TILEB];
-  __shared__ __align__(1024) unsigned char kt2[NB > 2 ? G::TILEB : 16];
-  __shared__ __align__(1024) unsigned char kt3[NB > 3 ? G::TILEB : 16];
+  __shared__ __align__(1024) unsigned char kt2[KB > 2 ? G::TILEB : 16];
   __shared__ __align__(1024) unsigned char yt0[G::TILEB];
   __shared__ __align__(1024) unsigned char yt1[G::TILEB];
-  __shared__ __align__(1024) unsigned char yt2[NB > 2 ? G::TILEB : 16];
-  __shared__ __align__(1024) unsigned char yt3[NB > 3 ? G::TILEB : 16];
-  auto kbuf = [&](int j) -> unsigned char * { return j == 0 ? kt0 : j == 1 ? kt1 : j == 2 ? kt2 : kt3; };
-  auto ybuf = [&](int j) -> unsigned char * { return j == 0 ? yt0 : j == 1 ? yt1 : j == 2 ? yt2 : yt3; };
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
@@ -356,58 +362,74 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   bf16x8_t qb[G::DK];
   load_query<D>(qh, qgeo, qm, half, qb);
 
-  // (queries were requested first, so the first tile's wait also covers them)
   const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
-  auto issue = [&](int32_t t, int j) {
-    dma_tile<D, false>(kbytes, kbuf(j), geo, t * kKeyTile, wave, lane, NW);
-    dma_tile<D, false>(vbytes, ybuf(j), geo, t * kKeyTile, wave, lane, NW);
-  };
-#pragma unroll
-  for (int j = 0; j < PD; ++j)
-    if (j < n) issue(j, j);
+  // prologue: K(0..PK-1) and Y(0) (queries were requested first)
+  dma_tile<D, false>(kbytes, kt0, geo, 0, wave, lane, NW);
+  if (PK > 1 && n > 1) dma_tile<D, false>(kbytes, kt1, geo, kKeyTile, wave, lane, NW);
+  dma_tile<D, false>(vbytes, yt0, geo, 0, wave, lane, NW);
 
   f32x16_t oacc[G::DB];
 #pragma unroll
   for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int32_t t0 = 0; t0 < n; t0 += NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int32_t t = t0 + j;
-      if (t >= n) break;
-      const int32_t after = min(PD - 1, n - 1 - t);   // tiles issued after t, maybe in flight
-      if (after <= 0) wait_vmcnt<0>();
-      else if (after == 1) wait_vmcnt<PER_TILE>();
-      else wait_vmcnt<2 * PER_TILE>();
-      __syncthreads();   // tile t visible to all waves; buffer (j + PD) % NB no longer read
-      const bool more = t + PD < n;
-      const int jn = (j + PD) % NB;
-      const int32_t kn0 = (t + PD) * kKeyTile;
-      // This wave's DMA windows are wave, wave + NW, ...: WPT of them per
-      // tensor, spread evenly over the QK batches (keys) and the PV d-blocks
-      // (values); any left over go out after the tile.
-      constexpr int WPT = G::NINST / NW;
-      constexpr int NQ = 2 * (G::DK < 4 ? 1 : G::DK / 4);   // QK hook points per tile
-      constexpr int NP = 2 * G::DB;                          // PV hook points per tile
-      constexpr int SQ = NQ >= WPT ? NQ / WPT : 1, SP = NP >= WPT ? NP / WPT : 1;
-      auto on_qk = [&](int i) {
-        if (more && i % SQ == 0 && i / SQ < WPT) dma_window<D>(kbytes, kbuf(jn), geo, kn0, wave + NW * (i / SQ), lane);
-      };
-      auto on_pv = [&](int i) {
-        if (more && i % SP == 0 && i / SP < WPT) dma_window<D>(vbytes, ybuf(jn), geo, kn0, wave + NW * (i / SP), lane);
-      };
-      if (wave_active) {
-        attend_tile<D>(kbuf(j), ybuf(j), qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col,
-                       half, tr_key, tr_col, on_qk, on_pv);
-        if (more) {   // windows left over when there are fewer hook points than windows
-          for (int w = NQ / SQ; w < WPT; ++w) dma_window<D>(kbytes, kbuf(jn), geo, kn0, wave + NW * w, lane);
-          for (int w = NP / SP; w < WPT; ++w) dma_window<D>(vbytes, ybuf(jn), geo, kn0, wave + NW * w, lane);
-        }
-      } else if (more) {
-        dma_tile<D, false>(kbytes, kbuf(jn), geo, kn0, wave, lane, NW);
-        dma_tile<D, false>(vbytes, ybuf(jn), geo, kn0, wave, lane, NW);
-      }
+  constexpr int NQ = 2 * (G::DK < 4 ? 1 : G::DK / 4);   // QK hook points per tile
+  constexpr int NP = 2 * G::DB;                          // PV hook points per tile
+  constexpr int SQ = NQ >= WPT ? NQ / WPT : 1, SP = NP >= WPT ? NP / WPT : 1;
+
+  // One tile: computes from (kc, yc) and fills (yn, kn). Every call below
+  // passes distinct LDS objects, so the compiler can prove that a DMA in
+  // flight never aliases the buffers being read and adds no waits of its own.
+  auto step = [&](int32_t t, const unsigned char *kc, const unsigned char *yc, unsigned char *yn,
+                  unsigned char *kn) __attribute__((always_inline)) {
+    // Outstanding DMAs that tile t does not need: the key windows of tile
+    // t+PK-1, issued after the value windows of tile t (KB = 3 only).
+    if (PK > 1 && t > 0 && t + PK - 1 < n) wait_vmcnt<WPT>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // tile t visible; buffers of tiles t-1 (values) and t+PK-KB (keys) free
+    const bool y_more = t + 1 < n, k_more = t + PK < n;
+    const int32_t yk0 = (t + 1) * kKeyTile, kk0 = (t + PK) * kKeyTile;
+    auto on_qk = [&](int i) {
+      if (y_more && i % SQ == 0 && i / SQ < WPT) dma_window<D>(vbytes, yn, geo, yk0, wave + NW * (i / SQ), lane);
+    };
+    auto on_pv = [&](int i) {
+      if (k_more && i % SP == 0 && i / SP < WPT) dma_window<D>(kbytes, kn, geo, kk0, wave + NW * (i / SP), lane);
+    };
+    if (wave_active) {
+      // Windows beyond the hook points: value windows go out first (every
+      // value window of tile t+1 must precede the key windows of tile t+PK in
+      // issue order for the wait above), key windows after the tile.
+      if (y_more)
+        for (int w = NQ / SQ; w < WPT; ++w) dma_window<D>(vbytes, yn, geo, yk0, wave + NW * w, lane);
+      attend_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key,
+                     tr_col, on_qk, on_pv);
+      if (k_more)
+        for (int w = NP / SP; w < WPT; ++w) dma_window<D>(kbytes, kn, geo, kk0, wave + NW * w, lane);
+    } else {
+      if (y_more) dma_tile<D, false>(vbytes, yn, geo, yk0, wave, lane, NW);
+      if (k_more) dma_tile<D, false>(kbytes, kn, geo, kk0, wave, lane, NW);
+    }
+  };
+  // tile t: keys in kt[t % KB], values in yt[t % 2]; fills yt[(t+1) % 2], kt[(t+PK) % KB]
+  if constexpr (KB == 3) {
+    for (int32_t t = 0; t < n; t += 6) {
+      step(t, kt0, yt0, yt1, kt2);
+      if (t + 1 >= n) break;
+      step(t + 1, kt1, yt1, yt0, kt0);
+      if (t + 2 >= n) break;
+      step(t + 2, kt2, yt0, yt1, kt1);
+      if (t + 3 >= n) break;
+      step(t + 3, kt0, yt1, yt0, kt2);
+      if (t + 4 >= n) break;
+      step(t + 4, kt1, yt0, yt1, kt0);
+      if (t + 5 >= n) break;
+      step(t + 5, kt2, yt1, yt0, kt1);
+    }
+  } else {
+    for (int32_t t = 0; t < n; t += 2) {
+      step(t, kt0, yt0, yt1, kt1);
+      if (t + 1 >= n) break;
+      step(t + 1, kt1, yt1, yt0, kt0);
     }
   }
 
