@@ -115,19 +115,6 @@ __device__ __forceinline__ void dma_tile(const unsigned char *src, unsigned char
   }
 }
 
-// One DMA instruction (1 KB window ii) of a tile; see dma_tile.
-template <int D>
-__device__ __forceinline__ void dma_window(const unsigned char *src, unsigned char *dst, const GroupGeom &geo,
-                                           int32_t k0, int ii, int lane) {
-  using G = TileGeo<D>;
-  const int slot = ii * 64 + lane;
-  const int r = slot / G::CPR, pos = slot % G::CPR;
-  const int c = swizzle_chunk<G::CPR>(r, pos);
-  const int32_t km = min(k0 + r, geo.len - 1);
-  const uint32_t off = ((uint32_t)member_token(geo, km) * D + c * 8) * 2u;
-  __builtin_amdgcn_global_load_lds((MA_GLOBAL void *)(src + off), (MA_LDS void *)(dst + ii * 1024), 16, 0, 0);
-}
-
 // This lane's query as the B operand of S^T = K Q^T: head_dim slots
 // [D/2*half + 8j, +8) for k-step j.
 template <int D>
@@ -305,29 +292,220 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // take part in the DMA and the barriers). Every wave reads the workgroup's
 // shared key/value tiles.
 //
-// Rings: key tiles in KB LDS buffers (tile t in buffer t % KB), value tiles in
-// two (t % 2). While computing tile t a wave issues the value windows of tile
-// t+1 right after its QK MFMA batches, and the key windows of tile t+KB-1
-// after its PV d-blocks, one DMA instruction at a time. The barrier opening
-// tile t+1 therefore waits only for DMAs issued about a tile earlier (values)
-// or two tiles earlier (keys, KB = 3). Vector-memory loads retire in order, so
-// the wait may leave the newest key windows in flight.
+// Rings: key tiles in three LDS buffers (tile t in buffer t % 3), value tiles
+// in two (t % 2). While computing tile t a wave issues the value windows of
+// tile t+1 between its QK MFMAs and the key windows of tile t+2 between its
+// PV MFMAs, one DMA instruction at a time. Vector-memory loads retire in
+// order, so the wait that opens tile t can leave the newest key windows
+// (tile t+1) in flight. DMAs for tiles past the group are issued anyway from
+// clamped rows (the last member, one cache line per row) into buffers no wave
+// reads again: the tile loop then has no data-dependent branches, and the
+// per-wave count of outstanding DMAs is the same at every tile.
+
+// Token of group member m for the DMA address: base + (m / len_i) * stride_out
+// + (m % len_i) * stride_in. The quotient uses a double reciprocal: for
+// 0 <= m < 2^31 the truncated product m * (1/len_i) is within 2^-21 of m/len_i
+// relative to 1/len_i, so it is the exact quotient or, when len_i divides m,
+// one less; the remainder test repairs that. One-level groups have
+// len_i = len > m, so the quotient is 0 there.
+struct RowMap {
+  int32_t base, len_i, stride_in, stride_out, last;
+  double rcp;
+};
+
+__device__ __forceinline__ RowMap row_map(const GroupGeom &g) {
+  RowMap r;
+  r.base = g.base;
+  r.len_i = g.len_i;
+  r.stride_in = g.stride_in;
+  r.stride_out = g.stride_out;
+  r.last = g.len - 1;
+  r.rcp = 1.0 / (double)g.len_i;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t row_token(const RowMap &rm, int32_t m) {
+  int32_t o = (int32_t)((double)m * rm.rcp);
+  int32_t x = m - o * rm.len_i;
+  const bool up = x >= rm.len_i;
+  o += up ? 1 : 0;
+  x -= up ? rm.len_i : 0;
+  return (uint32_t)(rm.base + o * rm.stride_out + x * rm.stride_in);
+}
+
+// One global_load_lds_dwordx4 (lane l: 16 bytes from src + off_l to LDS
+// lds_dst + 16 l), written as inline assembly. The compiler's wait insertion
+// models the builtin form as a FLAT access that may also complete through the
+// LDS counter, out of order, and then makes every wait for an LDS read a full
+// lgkmcnt(0), which stalls each MFMA on the reads issued ahead for the next
+// one. The streaming kernel orders its DMAs with explicit vmcnt waits and
+// barriers instead, so the compiler need not see them. No register is
+// written: the instruction only reads its address operands at issue.
+__device__ __forceinline__ void dma16(const unsigned char *src, uint32_t off, unsigned char *lds_dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(MA_LDS unsigned char *)lds_dst;
+  // s_nop: one wait state between the M0 write and the DMA that reads it
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(src), "{m0}"(lds_addr) : "memory");
+}
+
+// A workgroup-uniform pointer, held in scalar registers (the DMA's base operand).
+__device__ __forceinline__ const unsigned char *uniform_ptr(const unsigned char *p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  // readfirstlane returns int: go through uint32_t so the low word is not sign-extended
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const unsigned char *>((uintptr_t)((hi << 32) | lo));
+}
+
+// DMA window ii (1 KB: 64 lanes x 16 bytes) of the tile holding group rows
+// [k0, k0 + 64); rows past the group repeat its last member.
+template <int D>
+__device__ __forceinline__ void dma_row_window(const unsigned char *src, unsigned char *dst, const RowMap &rm,
+                                               int32_t k0, int ii, int lane) {
+  using G = TileGeo<D>;
+  const int slot = ii * 64 + lane;
+  const int r = slot / G::CPR, pos = slot % G::CPR;
+  const int c = swizzle_chunk<G::CPR>(r, pos);
+  const int32_t km = min(k0 + r, rm.last);
+  // offsets inside one (batch, head) slice fit in 32 bits (N * D < 2^31 elements)
+  const uint32_t off = (row_token(rm, km) * D + c * 8) * 2u;
+  dma16(src, off, dst + ii * 1024);
+}
+
+// Two softmax weights (scores s[r], s[r+1]) of this lane's query: exp2 of the
+// scaled score minus the running max, packed to bf16 into the P^T operand.
+__device__ __forceinline__ void exp_pair(const f32x16_t &s, int r, float scale_log2, float m_run, float &lsum,
+                                         bf16x8_t (&pb)[2]) {
+  const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
+  const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], scale_log2, -m_run));
+  lsum += e0 + e1;
+  const bf16x2_t pr = __builtin_convertvector((f32x2_t){e0, e1}, bf16x2_t);   // v_cvt_pk_bf16_f32
+  pb[r / 8][r % 8] = pr[0];
+  pb[r / 8][r % 8 + 1] = pr[1];
+}
+
+// One 64-key tile in a fixed instruction order. Scheduling barriers split the
+// tile into slots of one or two MFMAs each, so the compiler keeps the LDS
+// reads two MFMA slots ahead of their use (it would otherwise sink every read
+// next to its MFMA and wait for it there) and places the work listed per slot:
+//   QK slots j = 0..DK-1:    S^T of both 32-key blocks at k-step j, key
+//                            fragments of k-step j+2, on_qk(j)
+//   softmax:                 mask, tile max, one lazy-rescale decision for
+//                            the whole tile, weights of block 0
+//   PV slots i = 0..4DB-1:   one O^T += Y^T P^T step, value fragments of step
+//                            i+2, on_pv(i); during block 0's steps also the
+//                            weights of block 1, two scores per slot (DB = 4)
+// One rescale decision per tile (instead of per 32-key block) keeps block 1's
+// weights free of any write to the accumulators that block 0's MFMAs update.
+template <int D, typename FQ, typename FP>
+__device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsigned char *vs,
+                                            const bf16x8_t *qb, int32_t k0, int32_t len, float scale_log2,
+                                            float &m_run, float &l_run, f32x16_t *oacc, int col, int half,
+                                            int tr_key, int tr_col, FQ &&on_qk, FP &&on_pv) {
+  using G = TileGeo<D>;
+  constexpr int DK = G::DK, DB = G::DB;
+  constexpr int AK = DK < 2 ? DK : 2;   // k-steps of key fragments in flight
+  const int r0 = col, r1 = 32 + col;
+  bf16x8_t kf0[DK], kf1[DK];
+  auto read_k = [&](int j) __attribute__((always_inline)) {
+    const int c = DK * half + j;
+    kf0[j] = *reinterpret_cast<const bf16x8_t *>(ks + r0 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r0, c));
+    kf1[j] = *reinterpret_cast<const bf16x8_t *>(ks + r1 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r1, c));
+  };
+#pragma unroll
+  for (int j = 0; j < AK; ++j) read_k(j);
+  f32x16_t s0 = {}, s1 = {};
+#pragma unroll
+  for (int j = 0; j < DK; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0[j], qb[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[j], qb[j], s1, 0, 0, 0);
+    if (j + AK < DK) read_k(j + AK);
+    on_qk(j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- softmax of the tile: scores r of this lane are keys k0 + 8(r/4) + 4half + r%4 (+32 in s1)
+  if (k0 + 64 > len) {   // ragged tile: keys past the group get -inf
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t key = k0 + 8 * (r / 4) + 4 * half + (r % 4);
+      if (key >= len) s0[r] = -INFINITY;
+      if (key + 32 >= len) s1[r] = -INFINITY;
+    }
+  }
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, swap_halves(mx));   // the other 16 keys of each block for this query
+  const float tmax = mx * scale_log2;
+  if (__any(tmax > m_run + kLazyRescale)) {
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    m_run = m_new;
+  }
+  float lsum = 0.f;
+  bf16x8_t p0[2], p1[2];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) exp_pair(s0, r, scale_log2, m_run, lsum, p0);
+
+  // ---- O^T += Y^T P^T: step i covers block kb = i / 2DB, keys +16h (h = i / DB % 2), d-block b = i % DB
+  constexpr int NPV = 4 * DB;
+  constexpr int AV = 2;                            // steps of value fragments in flight
+  constexpr int EPS = 16 / (2 * DB);               // block-1 scores converted per block-0 step
+  bf16x8_t yf[NPV];
+  auto read_y = [&](int i) __attribute__((always_inline)) {
+    const int kb = i / (2 * DB), h = (i / DB) & 1, b = i % DB;
+    const int ra = 32 * kb + 16 * h + tr_key;
+    const int rb = ra + 8;
+    // head_dim column of this lane's source run; past head_dim (D = 16 only)
+    // the whole 16-lane group reads column 0 and feeds zero rows instead.
+    const int cidx = 32 * b + tr_col;
+    const bool dvalid = (G::DB * 32 == D) || cidx < D;
+    const int cc = dvalid ? cidx : 0;
+    const unsigned char *pa = vs + ra * G::ROWB + 16 * swizzle_chunk<G::CPR>(ra, cc >> 3) + 2 * (cc & 7);
+    const unsigned char *pbp = vs + rb * G::ROWB + 16 * swizzle_chunk<G::CPR>(rb, cc >> 3) + 2 * (cc & 7);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)pa);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)pbp);
+    yf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if (!dvalid) yf[i] = bf16x8_t{};
+  };
+#pragma unroll
+  for (int i = 0; i < AV; ++i) read_y(i);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int kb = i / (2 * DB), h = (i / DB) & 1, b = i % DB;
+    oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yf[i], kb ? p1[h] : p0[h], oacc[b], 0, 0, 0);
+    if (i + AV < NPV) read_y(i + AV);
+    if (i < 2 * DB) {
+#pragma unroll
+      for (int e = 0; e < EPS; e += 2) exp_pair(s1, EPS * i + e, scale_log2, m_run, lsum, p1);
+    }
+    on_pv(i);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  l_run += lsum;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int NW, int KB>
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
-  static_assert(KB == 2 || KB == 3, "key ring of 2 or 3 buffers");
-  constexpr int PK = KB - 1;                 // key tiles issued ahead
   constexpr int WPT = G::NINST / NW;         // DMA windows per tile, tensor and wave
   __shared__ __align__(1024) unsigned char kt0[G::TILEB];
   __shared__ __align__(1024) unsigned char kt1[G::TILEB];
-  __shared__ __align__(1024) unsigned char kt2[KB > 2 ? G::TILEB : 16];
+  __shared__ __align__(1024) unsigned char kt2[G::TILEB];
   __shared__ __align__(1024) unsigned char yt0[G::TILEB];
   __shared__ __align__(1024) unsigned char yt1[G::TILEB];
 
@@ -340,12 +518,13 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int32_t qbase = qt * p.q_tile;
   if (qbase >= geo.len) return;   // uniform over the workgroup
   const int32_t qend = min(geo.len, qbase + p.q_tile);
+  const RowMap rm = row_map(geo);
 
   const u16 *qh = static_cast<const u16 *>(p.q) + bh * p.head_elems;
-  const unsigned char *kbytes =
-      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + bh * p.head_elems);
-  const unsigned char *vbytes =
-      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + bh * p.head_elems);
+  const unsigned char *kbytes = uniform_ptr(
+      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + bh * p.head_elems));
+  const unsigned char *vbytes = uniform_ptr(
+      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + bh * p.head_elems));
   u16 *oh = static_cast<u16 *>(p.out) + bh * p.head_elems;
 
   const int lane = threadIdx.x & 63;
@@ -363,76 +542,76 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   load_query<D>(qh, qgeo, qm, half, qb);
 
   const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
-  // prologue: K(0..PK-1) and Y(0) (queries were requested first)
-  dma_tile<D, false>(kbytes, kt0, geo, 0, wave, lane, NW);
-  if (PK > 1 && n > 1) dma_tile<D, false>(kbytes, kt1, geo, kKeyTile, wave, lane, NW);
-  dma_tile<D, false>(vbytes, yt0, geo, 0, wave, lane, NW);
+  // prologue, in the order the first wait relies on: K(0), Y(0), K(1)
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kt0, rm, 0, wave + NW * w, lane);
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) dma_row_window<D>(vbytes, yt0, rm, 0, wave + NW * w, lane);
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kt1, rm, kKeyTile, wave + NW * w, lane);
+  // The compiler does not see the DMAs above; make its wait for the query
+  // loads happen here, once, rather than at their first use inside the loop
+  // (where its loop-carried state would put a vmcnt(0) in every iteration).
+#pragma unroll
+  for (int j = 0; j < G::DK; ++j) asm volatile("" ::"v"(qb[j]));
 
   f32x16_t oacc[G::DB];
 #pragma unroll
   for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  constexpr int NQ = 2 * (G::DK < 4 ? 1 : G::DK / 4);   // QK hook points per tile
-  constexpr int NP = 2 * G::DB;                          // PV hook points per tile
+  constexpr int NQ = G::DK;        // QK hook points per tile
+  constexpr int NP = 4 * G::DB;    // PV hook points per tile
   constexpr int SQ = NQ >= WPT ? NQ / WPT : 1, SP = NP >= WPT ? NP / WPT : 1;
+  constexpr int XQ = NQ / SQ < WPT ? NQ / SQ : WPT, XP = NP / SP < WPT ? NP / SP : WPT;   // windows in hooks
 
   // One tile: computes from (kc, yc) and fills (yn, kn). Every call below
   // passes distinct LDS objects, so the compiler can prove that a DMA in
   // flight never aliases the buffers being read and adds no waits of its own.
   auto step = [&](int32_t t, const unsigned char *kc, const unsigned char *yc, unsigned char *yn,
                   unsigned char *kn) __attribute__((always_inline)) {
-    // Outstanding DMAs that tile t does not need: the key windows of tile
-    // t+PK-1, issued after the value windows of tile t (KB = 3 only).
-    if (PK > 1 && t > 0 && t + PK - 1 < n) wait_vmcnt<WPT>();
-    else wait_vmcnt<0>();
-    __syncthreads();   // tile t visible; buffers of tiles t-1 (values) and t+PK-KB (keys) free
-    const bool y_more = t + 1 < n, k_more = t + PK < n;
-    const int32_t yk0 = (t + 1) * kKeyTile, kk0 = (t + PK) * kKeyTile;
-    auto on_qk = [&](int i) {
-      if (y_more && i % SQ == 0 && i / SQ < WPT) dma_window<D>(vbytes, yn, geo, yk0, wave + NW * (i / SQ), lane);
-    };
-    auto on_pv = [&](int i) {
-      if (k_more && i % SP == 0 && i / SP < WPT) dma_window<D>(kbytes, kn, geo, kk0, wave + NW * (i / SP), lane);
-    };
+    // Outstanding: ... Y(t), K(t+1); tile t needs everything but K(t+1).
+    wait_vmcnt<WPT>();
+    __syncthreads();   // tile t visible; buffers of tiles t-1 (values) and t-1 (keys) free
+    const int32_t yk0 = (t + 1) * kKeyTile, kk0 = (t + 2) * kKeyTile;
     if (wave_active) {
-      // Windows beyond the hook points: value windows go out first (every
-      // value window of tile t+1 must precede the key windows of tile t+PK in
-      // issue order for the wait above), key windows after the tile.
-      if (y_more)
-        for (int w = NQ / SQ; w < WPT; ++w) dma_window<D>(vbytes, yn, geo, yk0, wave + NW * w, lane);
-      attend_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key,
+      // value windows of tile t+1 precede the key windows of tile t+2 in issue order
+#pragma unroll
+      for (int w = XQ; w < WPT; ++w) dma_row_window<D>(vbytes, yn, rm, yk0, wave + NW * w, lane);
+      auto on_qk = [&](int i) __attribute__((always_inline)) {
+        if (i % SQ == 0 && i / SQ < XQ) dma_row_window<D>(vbytes, yn, rm, yk0, wave + NW * (i / SQ), lane);
+      };
+      auto on_pv = [&](int i) __attribute__((always_inline)) {
+        if (i % SP == 0 && i / SP < XP) dma_row_window<D>(kbytes, kn, rm, kk0, wave + NW * (i / SP), lane);
+      };
+      stream_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key,
                      tr_col, on_qk, on_pv);
-      if (k_more)
-        for (int w = NP / SP; w < WPT; ++w) dma_window<D>(kbytes, kn, geo, kk0, wave + NW * w, lane);
+#pragma unroll
+      for (int w = XP; w < WPT; ++w) dma_row_window<D>(kbytes, kn, rm, kk0, wave + NW * w, lane);
     } else {
-      if (y_more) dma_tile<D, false>(vbytes, yn, geo, yk0, wave, lane, NW);
-      if (k_more) dma_tile<D, false>(kbytes, kn, geo, kk0, wave, lane, NW);
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) dma_row_window<D>(vbytes, yn, rm, yk0, wave + NW * w, lane);
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kn, rm, kk0, wave + NW * w, lane);
     }
   };
-  // tile t: keys in kt[t % KB], values in yt[t % 2]; fills yt[(t+1) % 2], kt[(t+PK) % KB]
-  if constexpr (KB == 3) {
-    for (int32_t t = 0; t < n; t += 6) {
-      step(t, kt0, yt0, yt1, kt2);
-      if (t + 1 >= n) break;
-      step(t + 1, kt1, yt1, yt0, kt0);
-      if (t + 2 >= n) break;
-      step(t + 2, kt2, yt0, yt1, kt1);
-      if (t + 3 >= n) break;
-      step(t + 3, kt0, yt1, yt0, kt2);
-      if (t + 4 >= n) break;
-      step(t + 4, kt1, yt0, yt1, kt0);
-      if (t + 5 >= n) break;
-      step(t + 5, kt2, yt1, yt0, kt1);
-    }
-  } else {
-    for (int32_t t = 0; t < n; t += 2) {
-      step(t, kt0, yt0, yt1, kt1);
-      if (t + 1 >= n) break;
-      step(t + 1, kt1, yt1, yt0, kt0);
-    }
+  // tile t: keys in kt[t % 3], values in yt[t % 2]; fills yt[(t+1) % 2], kt[(t+2) % 3]
+  for (int32_t t = 0; t < n; t += 6) {
+    step(t, kt0, yt0, yt1, kt2);
+    if (t + 1 >= n) break;
+    step(t + 1, kt1, yt1, yt0, kt0);
+    if (t + 2 >= n) break;
+    step(t + 2, kt2, yt0, yt1, kt1);
+    if (t + 3 >= n) break;
+    step(t + 3, kt0, yt1, yt0, kt2);
+    if (t + 4 >= n) break;
+    step(t + 4, kt1, yt0, yt1, kt0);
+    if (t + 5 >= n) break;
+    step(t + 5, kt2, yt1, yt0, kt1);
   }
-
+  // DMAs into buffers past the last tile may still be in flight; they must
+  // land before the workgroup's LDS is handed to another workgroup.
+  wait_vmcnt<0>();
   if (qm < qend) store_row<D>(oh + (uint32_t)member_token(geo, qm) * D, oacc, l_run, half);
 }
 

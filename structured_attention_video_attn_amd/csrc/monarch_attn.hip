@@ -82,11 +82,11 @@ int launch_d(const Plan &pl, hipStream_t s) {
       // waves per workgroup; every wave must issue whole DMA instructions
       if constexpr (TileGeo<D>::NINST % 4 == 0) {
         if (pl.waves >= 4) {
-          hipLaunchKernelGGL((group_attn_bf16<D, 4, 3>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
+          hipLaunchKernelGGL((group_attn_bf16<D, 4>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
           break;
         }
       }
-      hipLaunchKernelGGL((group_attn_bf16<D, 2, 3>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
+      hipLaunchKernelGGL((group_attn_bf16<D, 2>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
       break;
   }
   return hip_status(hipGetLastError());
