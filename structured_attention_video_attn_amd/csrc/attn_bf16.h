@@ -498,7 +498,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int NW>
+template <int D, int NW, bool kTwoLevel>
 __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
@@ -533,6 +533,34 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int tr_key = 4 * half + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // DMA window w (of this wave's WPT per tile and tensor) of the tile holding
+  // group rows [k0, k0 + 64). One-level groups (a member's token is
+  // base + m * stride_in) take the offset with one 24-bit multiply-add; the
+  // host picks this form only when members and the member stride in bytes fit
+  // in 24 bits. Two-level groups (tiled boxes) go through row_token.
+  using G0 = TileGeo<D>;
+  constexpr int WPT0 = G0::NINST / NW;
+  const int lane_row = lane / G0::CPR;
+  const uint32_t mstride = (uint32_t)rm.stride_in * (2u * D);   // bytes between consecutive members
+  uint32_t csb[WPT0];   // byte offset of member 0's row plus this lane's swizzled chunk, per window
+#pragma unroll
+  for (int w = 0; w < WPT0; ++w) {
+    const int ii = wave + NW * w;
+    const int slot = ii * 64 + lane;
+    const int r = slot / G0::CPR, pos = slot % G0::CPR;
+    csb[w] = (uint32_t)rm.base * (2u * D) + 16u * (uint32_t)swizzle_chunk<G0::CPR>(r, pos);
+  }
+  auto window = [&](const unsigned char *src, unsigned char *dst, int32_t k0, int w)
+                    __attribute__((always_inline)) {
+    const int ii = wave + NW * w;
+    if constexpr (kTwoLevel) {
+      dma_row_window<D>(src, dst, rm, k0, ii, lane);
+    } else {
+      const int32_t km = min(lane_row + (k0 + ii * G0::ROWS_PER_INST), rm.last);
+      dma16(src, __umul24((uint32_t)km, mstride) + csb[w], dst + ii * 1024);
+    }
+  };
+
   const int32_t q0 = qbase + wave * kQueriesPerWave;
   const int32_t qm = q0 + col;
   const bool wave_active = q0 < qend;   // wave-uniform
@@ -544,11 +572,11 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
   // prologue, in the order the first wait relies on: K(0), Y(0), K(1)
 #pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kt0, rm, 0, wave + NW * w, lane);
+  for (int w = 0; w < WPT; ++w) window(kbytes, kt0, 0, w);
 #pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(vbytes, yt0, rm, 0, wave + NW * w, lane);
+  for (int w = 0; w < WPT; ++w) window(vbytes, yt0, 0, w);
 #pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kt1, rm, kKeyTile, wave + NW * w, lane);
+  for (int w = 0; w < WPT; ++w) window(kbytes, kt1, kKeyTile, w);
   // The compiler does not see the DMAs above; make its wait for the query
   // loads happen here, once, rather than at their first use inside the loop
   // (where its loop-carried state would put a vmcnt(0) in every iteration).
@@ -577,22 +605,22 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
     if (wave_active) {
       // value windows of tile t+1 precede the key windows of tile t+2 in issue order
 #pragma unroll
-      for (int w = XQ; w < WPT; ++w) dma_row_window<D>(vbytes, yn, rm, yk0, wave + NW * w, lane);
+      for (int w = XQ; w < WPT; ++w) window(vbytes, yn, yk0, w);
       auto on_qk = [&](int i) __attribute__((always_inline)) {
-        if (i % SQ == 0 && i / SQ < XQ) dma_row_window<D>(vbytes, yn, rm, yk0, wave + NW * (i / SQ), lane);
+        if (i % SQ == 0 && i / SQ < XQ) window(vbytes, yn, yk0, (i / SQ));
       };
       auto on_pv = [&](int i) __attribute__((always_inline)) {
-        if (i % SP == 0 && i / SP < XP) dma_row_window<D>(kbytes, kn, rm, kk0, wave + NW * (i / SP), lane);
+        if (i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
       stream_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key,
                      tr_col, on_qk, on_pv);
 #pragma unroll
-      for (int w = XP; w < WPT; ++w) dma_row_window<D>(kbytes, kn, rm, kk0, wave + NW * w, lane);
+      for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);
     } else {
 #pragma unroll
-      for (int w = 0; w < WPT; ++w) dma_row_window<D>(vbytes, yn, rm, yk0, wave + NW * w, lane);
+      for (int w = 0; w < WPT; ++w) window(vbytes, yn, yk0, w);
 #pragma unroll
-      for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kn, rm, kk0, wave + NW * w, lane);
+      for (int w = 0; w < WPT; ++w) window(kbytes, kn, kk0, w);
     }
   };
   // tile t: keys in kt[t % 3], values in yt[t % 2]; fills yt[(t+1) % 2], kt[(t+2) % 3]

@@ -37,6 +37,8 @@ struct Plan {
   uint32_t blocks;    // workgroups (the persistent kernel: an upper bound, see run_plan)
   int32_t n_items;    // groups * batch * heads (persistent kernel only)
   int32_t waves;      // waves per workgroup (streaming kernel only)
+  bool two_level;     // streaming kernel: some group spans several outer rows (tiled boxes), or
+                      // member offsets do not fit the 24-bit one-level DMA addressing
   Kernel kernel;
 };
 
@@ -82,11 +84,17 @@ int launch_d(const Plan &pl, hipStream_t s) {
       // waves per workgroup; every wave must issue whole DMA instructions
       if constexpr (TileGeo<D>::NINST % 4 == 0) {
         if (pl.waves >= 4) {
-          hipLaunchKernelGGL((group_attn_bf16<D, 4>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
+          if (pl.two_level)
+            hipLaunchKernelGGL((group_attn_bf16<D, 4, true>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
+          else
+            hipLaunchKernelGGL((group_attn_bf16<D, 4, false>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
           break;
         }
       }
-      hipLaunchKernelGGL((group_attn_bf16<D, 2>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
+      if (pl.two_level)
+        hipLaunchKernelGGL((group_attn_bf16<D, 2, true>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
+      else
+        hipLaunchKernelGGL((group_attn_bf16<D, 2, false>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
       break;
   }
   return hip_status(hipGetLastError());
@@ -129,6 +137,9 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
     pl->waves = w;
     q_per_block = (int)(kQueriesPerWave * need);
     pl->kernel = Kernel::kStream;
+    const bool outer = ga.len_o > 1 && ga.tile_o > 1;
+    const int64_t mstride = (int64_t)ga.stride_in * 2 * p.D;
+    pl->two_level = outer || ga.max_len >= (1 << 24) || mstride >= (1 << 24);
   }
   a.n_qtiles = (ga.max_len + q_per_block - 1) / q_per_block;
   a.q_tile = q_per_block;
