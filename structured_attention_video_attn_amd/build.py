@@ -34,6 +34,9 @@ def compile_flags():
         "-fPIC",
         "-shared",
         "-fno-strict-aliasing",
+        # no kernel relies on NaN semantics (masked scores are -inf): lets fmaxf
+        # map to one v_max/v_max3 without canonicalising its MFMA-produced inputs
+        "-fno-honor-nans",
         # keep the compiler from forming packed fp32 vector ops (v_pk_*_f32)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",

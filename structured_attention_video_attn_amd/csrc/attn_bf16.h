@@ -372,13 +372,15 @@ __device__ __forceinline__ void dma_row_window(const unsigned char *src, unsigne
 }
 
 // Two softmax weights (scores s[r], s[r+1]) of this lane's query: exp2 of the
-// scaled score minus the running max, packed to bf16 into the P^T operand.
+// scaled score minus the running max, packed to bf16 into the P^T operand and
+// added to the running sum.
 __device__ __forceinline__ void exp_pair(const f32x16_t &s, int r, float scale_log2, float m_run, float &lsum,
                                          bf16x8_t (&pb)[2]) {
   const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
   const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], scale_log2, -m_run));
-  lsum += e0 + e1;
   const bf16x2_t pr = __builtin_convertvector((f32x2_t){e0, e1}, bf16x2_t);   // v_cvt_pk_bf16_f32
+  // running sum of the rounded weights (the values the PV MFMA multiplies), one dot2 per pair
+  lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, (bf16x2_t){(__bf16)1.f, (__bf16)1.f}, lsum, false);
   pb[r / 8][r % 8] = pr[0];
   pb[r / 8][r % 8 + 1] = pr[1];
 }
