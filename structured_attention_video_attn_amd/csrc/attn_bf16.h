@@ -385,6 +385,38 @@ __device__ __forceinline__ void exp_pair(const f32x16_t &s, int r, float scale_l
   pb[r / 8][r % 8 + 1] = pr[1];
 }
 
+// Per-lane LDS byte offsets of the streaming tile's fragment reads, relative
+// to the tile buffer: computed once per kernel, so that each read is one
+// ds_read with the buffer (and row-block) base in its immediate offset. The
+// XOR swizzle of row r depends only on r mod (D/8), so value rows
+// 32kb + 16h + tr_key (+8) share the offsets of rows tr_key (+8).
+template <int D>
+struct LaneOffsets {
+  uint32_t k[TileGeo<D>::DK];        // key row col, chunk (D/16) half + j
+  uint32_t ya[TileGeo<D>::DB];       // value row tr_key, head_dim column 32b + tr_col
+  uint32_t yb[TileGeo<D>::DB];       // value row tr_key + 8, same column
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int col, int half, int tr_key, int tr_col) {
+  using G = TileGeo<D>;
+  LaneOffsets<D> o;
+#pragma unroll
+  for (int j = 0; j < G::DK; ++j)
+    o.k[j] = (uint32_t)(col * G::ROWB + 16 * swizzle_chunk<G::CPR>(col, G::DK * half + j));
+#pragma unroll
+  for (int b = 0; b < G::DB; ++b) {
+    // head_dim column of this lane's source run; past head_dim (D = 16 only)
+    // the whole 16-lane group reads column 0 (and the tile feeds zero rows).
+    const int cidx = 32 * b + tr_col;
+    const int cc = (G::DB * 32 == D) || cidx < D ? cidx : 0;
+    const int ra = tr_key, rb = tr_key + 8;
+    o.ya[b] = (uint32_t)(ra * G::ROWB + 16 * swizzle_chunk<G::CPR>(ra, cc >> 3) + 2 * (cc & 7));
+    o.yb[b] = (uint32_t)(rb * G::ROWB + 16 * swizzle_chunk<G::CPR>(rb, cc >> 3) + 2 * (cc & 7));
+  }
+  return o;
+}
+
 // One 64-key tile in a fixed instruction order. Scheduling barriers split the
 // tile into slots of one or two MFMAs each, so the compiler keeps the LDS
 // reads two MFMA slots ahead of their use (it would otherwise sink every read
@@ -401,17 +433,16 @@ __device__ __forceinline__ void exp_pair(const f32x16_t &s, int r, float scale_l
 template <int D, typename FQ, typename FP>
 __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsigned char *vs,
                                             const bf16x8_t *qb, int32_t k0, int32_t len, float scale_log2,
-                                            float &m_run, float &l_run, f32x16_t *oacc, int col, int half,
-                                            int tr_key, int tr_col, FQ &&on_qk, FP &&on_pv) {
+                                            float &m_run, float &l_run, f32x16_t *oacc, int half, int tr_col,
+                                            const LaneOffsets<D> &lo, FQ &&on_qk, FP &&on_pv) {
   using G = TileGeo<D>;
   constexpr int DK = G::DK, DB = G::DB;
   constexpr int AK = DK < 2 ? DK : 2;   // k-steps of key fragments in flight
-  const int r0 = col, r1 = 32 + col;
   bf16x8_t kf0[DK], kf1[DK];
   auto read_k = [&](int j) __attribute__((always_inline)) {
-    const int c = DK * half + j;
-    kf0[j] = *reinterpret_cast<const bf16x8_t *>(ks + r0 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r0, c));
-    kf1[j] = *reinterpret_cast<const bf16x8_t *>(ks + r1 * G::ROWB + 16 * swizzle_chunk<G::CPR>(r1, c));
+    // rows col and 32 + col share the swizzle (32 is a multiple of D/8)
+    kf0[j] = *reinterpret_cast<const bf16x8_t *>(ks + lo.k[j]);
+    kf1[j] = *reinterpret_cast<const bf16x8_t *>(ks + 32 * G::ROWB + lo.k[j]);
   };
 #pragma unroll
   for (int j = 0; j < AK; ++j) read_k(j);
@@ -462,19 +493,12 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
   bf16x8_t yf[NPV];
   auto read_y = [&](int i) __attribute__((always_inline)) {
     const int kb = i / (2 * DB), h = (i / DB) & 1, b = i % DB;
-    const int ra = 32 * kb + 16 * h + tr_key;
-    const int rb = ra + 8;
-    // head_dim column of this lane's source run; past head_dim (D = 16 only)
-    // the whole 16-lane group reads column 0 and feeds zero rows instead.
-    const int cidx = 32 * b + tr_col;
-    const bool dvalid = (G::DB * 32 == D) || cidx < D;
-    const int cc = dvalid ? cidx : 0;
-    const unsigned char *pa = vs + ra * G::ROWB + 16 * swizzle_chunk<G::CPR>(ra, cc >> 3) + 2 * (cc & 7);
-    const unsigned char *pbp = vs + rb * G::ROWB + 16 * swizzle_chunk<G::CPR>(rb, cc >> 3) + 2 * (cc & 7);
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)pa);
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)pbp);
-    yf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    if (!dvalid) yf[i] = bf16x8_t{};
+    const unsigned char *rows = vs + (32 * kb + 16 * h) * G::ROWB;
+    const bf16x4_t ylo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)(rows + lo.ya[b]));
+    const bf16x4_t yhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MA_LDS bf16x4_t *)(rows + lo.yb[b]));
+    yf[i] = __builtin_shufflevector(ylo, yhi, 0, 1, 2, 3, 4, 5, 6, 7);
+    // past head_dim (D = 16 only) this d-block feeds zero rows
+    if (!((G::DB * 32 == D) || 32 * b + tr_col < D)) yf[i] = bf16x8_t{};
   };
 #pragma unroll
   for (int i = 0; i < AV; ++i) read_y(i);
@@ -505,11 +529,12 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
   constexpr int WPT = G::NINST / NW;         // DMA windows per tile, tensor and wave
-  __shared__ __align__(1024) unsigned char kt0[G::TILEB];
-  __shared__ __align__(1024) unsigned char kt1[G::TILEB];
-  __shared__ __align__(1024) unsigned char kt2[G::TILEB];
-  __shared__ __align__(1024) unsigned char yt0[G::TILEB];
-  __shared__ __align__(1024) unsigned char yt1[G::TILEB];
+  // One LDS array with the five tile buffers at fixed offsets (value ring
+  // first): the unrolled steps below address each buffer by a constant, which
+  // the fragment reads carry in their immediate offsets.
+  __shared__ __align__(1024) unsigned char lds[5 * G::TILEB];
+  unsigned char *const yt0 = lds, *const yt1 = lds + G::TILEB;
+  unsigned char *const kt0 = lds + 2 * G::TILEB, *const kt1 = lds + 3 * G::TILEB, *const kt2 = lds + 4 * G::TILEB;
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
@@ -563,6 +588,8 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
     }
   };
 
+  const LaneOffsets<D> lo = lane_offsets<D>(col, half, tr_key, tr_col);
+
   const int32_t q0 = qbase + wave * kQueriesPerWave;
   const int32_t qm = q0 + col;
   const bool wave_active = q0 < qend;   // wave-uniform
@@ -595,9 +622,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   constexpr int SQ = NQ >= WPT ? NQ / WPT : 1, SP = NP >= WPT ? NP / WPT : 1;
   constexpr int XQ = NQ / SQ < WPT ? NQ / SQ : WPT, XP = NP / SP < WPT ? NP / SP : WPT;   // windows in hooks
 
-  // One tile: computes from (kc, yc) and fills (yn, kn). Every call below
-  // passes distinct LDS objects, so the compiler can prove that a DMA in
-  // flight never aliases the buffers being read and adds no waits of its own.
+  // One tile: computes from (kc, yc) and fills (yn, kn).
   auto step = [&](int32_t t, const unsigned char *kc, const unsigned char *yc, unsigned char *yn,
                   unsigned char *kn) __attribute__((always_inline)) {
     // Outstanding: ... Y(t), K(t+1); tile t needs everything but K(t+1).
@@ -614,8 +639,8 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
       auto on_pv = [&](int i) __attribute__((always_inline)) {
         if (i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
-      stream_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key,
-                     tr_col, on_qk, on_pv);
+      stream_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
+                     on_qk, on_pv);
 #pragma unroll
       for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);
     } else {
