@@ -547,12 +547,12 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int32_t qend = min(geo.len, qbase + p.q_tile);
   const RowMap rm = row_map(geo);
 
-  const u16 *qh = static_cast<const u16 *>(p.q) + bh * p.head_elems;
+  const unsigned char *qbytes = uniform_ptr(
+      reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.q) + bh * p.head_elems));
   const unsigned char *kbytes = uniform_ptr(
       reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + bh * p.head_elems));
   const unsigned char *vbytes = uniform_ptr(
       reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + bh * p.head_elems));
-  u16 *oh = static_cast<u16 *>(p.out) + bh * p.head_elems;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -593,24 +593,36 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int32_t q0 = qbase + wave * kQueriesPerWave;
   const int32_t qm = q0 + col;
   const bool wave_active = q0 < qend;   // wave-uniform
-  GroupGeom qgeo = geo;
-  qgeo.len = qend;                       // queries past this workgroup's share load zeros
-  bf16x8_t qb[G::DK];
-  load_query<D>(qh, qgeo, qm, half, qb);
 
   const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
-  // prologue, in the order the first wait relies on: K(0), Y(0), K(1)
+  // Prologue. The workgroup's 32*NW query rows come in like key tiles (whole
+  // rows per DMA window, rather than 16 bytes of 64 rows per load) into the
+  // buffers of value tile 1 and key tile 2, which stay free until step 0
+  // refills them; then K(0), Y(0), K(1).
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) window(qbytes, yt1, qbase, w);
+  if constexpr (NW > 2) {
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) window(qbytes, kt2, qbase + kKeyTile, w);
+  }
 #pragma unroll
   for (int w = 0; w < WPT; ++w) window(kbytes, kt0, 0, w);
 #pragma unroll
   for (int w = 0; w < WPT; ++w) window(vbytes, yt0, 0, w);
 #pragma unroll
   for (int w = 0; w < WPT; ++w) window(kbytes, kt1, kKeyTile, w);
-  // The compiler does not see the DMAs above; make its wait for the query
-  // loads happen here, once, rather than at their first use inside the loop
-  // (where its loop-carried state would put a vmcnt(0) in every iteration).
+  wait_vmcnt<0>();
+  __syncthreads();
+  // This lane's query (row 32*wave + col of the query tile) as the B operand
+  // of S^T = K Q^T: the same fragments a key read of that row takes. Rows
+  // past the group or this workgroup's share hold other members' data; their
+  // results are never stored.
+  bf16x8_t qb[G::DK];
+  {
+    const unsigned char *qtile = (wave < 2 ? yt1 : kt2) + (wave & 1) * 32 * G::ROWB;
 #pragma unroll
-  for (int j = 0; j < G::DK; ++j) asm volatile("" ::"v"(qb[j]));
+    for (int j = 0; j < G::DK; ++j) qb[j] = *reinterpret_cast<const bf16x8_t *>(qtile + lo.k[j]);
+  }
 
   f32x16_t oacc[G::DB];
 #pragma unroll
@@ -665,9 +677,39 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
     step(t + 5, kt2, yt1, yt0, kt1);
   }
   // DMAs into buffers past the last tile may still be in flight; they must
-  // land before the workgroup's LDS is handed to another workgroup.
+  // land before the buffers are reused below (and before the workgroup's LDS
+  // is handed to another workgroup).
   wait_vmcnt<0>();
-  if (qm < qend) store_row<D>(oh + (uint32_t)member_token(geo, qm) * D, oacc, l_run, half);
+  __syncthreads();
+  // Output through LDS: each wave writes its normalised 32 x D tile row-major
+  // (16-byte chunks XOR-swizzled by row) into its own 32*2D bytes, then
+  // stores whole rows, D/8 lanes per row.
+  unsigned char *ot = lds + wave * 32 * G::ROWB;
+  {
+    const float inv = 1.f / (l_run + swap_halves(l_run));
+#pragma unroll
+    for (int b = 0; b < G::DB; ++b)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * b + 8 * rq + 4 * half;   // O^T element 4rq..4rq+3 of d-block b
+        if (d0 < D) {
+          bf16x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[b][4 * rq + e] * inv);
+          const int chunk = (d0 >> 3) ^ (col & (G::CPR - 1));
+          *reinterpret_cast<bf16x4_t *>(ot + col * G::ROWB + 16 * chunk + 8 * half) = v;
+        }
+      }
+  }
+  u16 *oh = static_cast<u16 *>(p.out) + bh * p.head_elems;
+  constexpr int RPI = 64 / G::CPR;   // rows per store instruction
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + lane / G::CPR, c = lane % G::CPR;
+    const uint4 v = *reinterpret_cast<const uint4 *>(ot + r * G::ROWB + 16 * (c ^ (r & (G::CPR - 1))));
+    const int32_t m = q0 + r;
+    if (m < qend) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(geo, m) * D + 8 * c) = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
