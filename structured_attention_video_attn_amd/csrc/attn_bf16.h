@@ -717,8 +717,9 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
 // w, w + G, w + 2G, ... (item = group + n_groups * (batch*head)); the keys and
 // values of item i+G go into the other LDS buffer pair, and its queries into
 // registers, while item i is computed. A wave waits for that prefetch only
-// right before its output stores, when it has had a whole item's compute to
-// land; the barrier opening the next item then publishes it to both waves.
+// after its compute, when it has had a whole item to land; the barrier opening
+// the next item then publishes it to both waves. Outputs leave through the
+// item's key buffer as whole rows rather than 8 bytes of 64 rows per store.
 template <int D>
 __global__ __launch_bounds__(kBlockWaves * 64, 2) void block_attn_bf16(AttnLaunch p, int32_t n_items) {
   using G = TileGeo<D>;
@@ -786,11 +787,33 @@ __global__ __launch_bounds__(kBlockWaves * 64, 2) void block_attn_bf16(AttnLaunc
     for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;
     attend_tile<D>(kc, yc, qb, 0, cur.geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key, tr_col);
-    const int32_t qm = wave * kQueriesPerWave + col;
-    wait_dma();   // the prefetch of `next` (and older stores) completed
-    if (qm < cur.geo.len) {
-      u16 *oh = static_cast<u16 *>(p.out) + cur.bh * p.head_elems;
-      store_row<D>(oh + (uint32_t)member_token(cur.geo, qm) * D, oacc, l_run, half);
+    wait_dma();        // the prefetch of `next` (and older stores) completed
+    __syncthreads();   // both waves are done with kc: it stages the output
+    // normalised 32 x D tile of this wave, row-major with XOR-swizzled
+    // chunks, then stored as whole rows (D/8 lanes per row)
+    unsigned char *ot = const_cast<unsigned char *>(kc) + wave * 32 * G::ROWB;
+    const float inv = 1.f / (l_run + swap_halves(l_run));
+#pragma unroll
+    for (int b = 0; b < G::DB; ++b)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * b + 8 * rq + 4 * half;
+        if (d0 < D) {
+          bf16x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[b][4 * rq + e] * inv);
+          const int chunk = (d0 >> 3) ^ (col & (G::CPR - 1));
+          *reinterpret_cast<bf16x4_t *>(ot + col * G::ROWB + 16 * chunk + 8 * half) = v;
+        }
+      }
+    u16 *oh = static_cast<u16 *>(p.out) + cur.bh * p.head_elems;
+    constexpr int RPI = 64 / G::CPR;   // rows per store instruction
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + lane / G::CPR, c = lane % G::CPR;
+      const uint4 v = *reinterpret_cast<const uint4 *>(ot + r * G::ROWB + 16 * (c ^ (r & (G::CPR - 1))));
+      const int32_t m = wave * kQueriesPerWave + r;
+      if (m < cur.geo.len) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(cur.geo, m) * D + 8 * c) = v;
     }
 #pragma unroll
     for (int j = 0; j < G::DK; ++j) qb[j] = qn[j];

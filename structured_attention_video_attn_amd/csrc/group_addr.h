@@ -42,7 +42,7 @@ struct GroupGeom {
   int32_t base;
   int32_t len_i;    // members along the inner axis in this group
   int32_t len;      // members in this group
-  bool two_level;   // len_o(g) > 1
+  int32_t two_level;   // len_o(g) > 1 (an int: GroupGeom has no padding bytes to copy)
   int32_t stride_in, stride_out;
 };
 
@@ -59,7 +59,7 @@ MA_HD GroupGeom group_geom(const GroupAddr &a, int32_t g) {
   r.base = w * a.stride_w + bi * a.tile_i * a.stride_in + bo * a.tile_o * a.stride_out;
   r.len_i = li;
   r.len = li * lo;
-  r.two_level = lo > 1;
+  r.two_level = lo > 1 ? 1 : 0;
   r.stride_in = a.stride_in;
   r.stride_out = a.stride_out;
   return r;
