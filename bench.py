@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,11 +57,16 @@ def parse_args():
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and whitespace removed (so that a
+    comment edit does not void counter data taken on unchanged code)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "structured_attention_video_attn_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,10 +11,10 @@
 //   group_attn_bf16  groups longer than 64 tokens (stage L, long stage-R
 //                    blocks, dense): a workgroup of 4 waves owns 128 queries
 //                    of one group and streams the group's keys and values
-//                    through LDS in 64-row tiles with an online softmax,
-//                    software-pipelined so that the S = QK^T products of
-//                    tile t+1 run on the matrix cores while the vector ALUs
-//                    do the softmax of tile t.
+//                    through LDS in 64-row tiles with an online softmax; each
+//                    tile runs in a fixed instruction order that keeps LDS
+//                    reads ahead of the MFMAs and puts the second 32-key
+//                    block's exponentials between the first block's PV MFMAs.
 //   block_attn_bf16  groups of at most 64 tokens (stage R's W-row blocks,
 //                    small tiles): persistent workgroups of 2 waves walk over
 //                    the groups and prefetch the next group's keys, values
@@ -25,9 +25,11 @@
 // (global_load_lds_dwordx4: lane l of an instruction fills LDS bytes
 // [16l, 16l+16) of that instruction's 1 KB window), row-major, 2*D bytes per
 // row, with the 16-byte chunks of row r permuted by an XOR swizzle so that
-// both read patterns below hit distinct LDS banks. Every buffer is its own
-// LDS object, so the compiler can prove that a DMA in flight never aliases
-// the buffer being read and does not wait for it.
+// both read patterns below hit distinct LDS banks. The block kernel's
+// buffers are separate LDS objects, so the compiler can prove that its
+// builtin DMAs in flight never alias the buffer being read; the streaming
+// kernel issues its DMAs through an inline-asm wrapper the compiler does not
+// track (see dma16) and orders them itself.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] B[16x32];
 // lane l holds A row l%32 and B column l%32, each with 8 k-slots 8*(l/32)+e;
