@@ -613,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   for (int w = 0; w < WPT; ++w) window(vbytes, yt0, 0, w);
 #pragma unroll
   for (int w = 0; w < WPT; ++w) window(kbytes, kt1, kKeyTile, w);
-  wait_vmcnt<0>();
+  wait_vmcnt<WPT>();   // everything but K(1), as at every later step
   __syncthreads();
   // This lane's query (row 32*wave + col of the query tile) as the B operand
   // of S^T = K Q^T: the same fragments a key read of that row takes. Rows
