@@ -231,6 +231,10 @@ def main():
         q, k, v, o, ws = sets[i % len(sets)]
         ma.monarch_attn_fwd(q, k, v, o, ws, T, H, W)
 
+    def step_r2(i):
+        q, k, v, o, ws = sets[i % len(sets)]
+        ma.monarch_attn_fwd(q, k, v, o, ws, T, H, W, r_axes=2)
+
     ms = time_loop(step, args.steps, args.warmup)
     ms_warm = time_loop(lambda i: step(0), args.steps, args.warmup)
 
@@ -284,7 +288,9 @@ def main():
         ms_tiled = time_loop(lambda i: ma.monarch_attn_tiled_fwd(q3, k3, v3, o3, ws3, T, H, W, tt, th),
                              args.steps, args.warmup)
         del q3, k3, v3, o3, ws3
-        q, k, v, o, _ = sets[0]
+        q, k, v, o, ws = sets[0]
+        # frame-aligned blocks (r_axes = 2): b2 = H*W = 1560, b1 = T = 21
+        ms_frames = time_loop(lambda i: step_r2(i), args.steps, args.warmup)
         ms_dense = time_loop(lambda i: ma.dense_attn_fwd(q, k, v, o), 3, 1)
         fr3, br3 = stage_work(N, d, heads, W)
         fl3, bl3 = stage_work(N, d, heads, tt * th)
@@ -293,6 +299,10 @@ def main():
             "tiled_structured_tokens_per_s": round(N / (ms_tiled * 1e-3), 1),
             "tiled_structured_roofline_frac": round(
                 (roofline_us(fr3, br3) + roofline_us(fl3, bl3)) / (ms_tiled * 1e3), 4),
+            "frame_blocks_ms": round(ms_frames, 4),
+            "frame_blocks_roofline_frac": round(
+                (roofline_us(*stage_work(N, d, heads, H * W)) + roofline_us(*stage_work(N, d, heads, T)))
+                / (ms_frames * 1e3), 4),
             "dense_ms": round(ms_dense, 3),
             "dense_tflops": round(4.0 * N * N * d * heads / (ms_dense * 1e-3) / 1e12, 1),
             "monarch_speedup_vs_dense": round(ms_dense / ms, 2),

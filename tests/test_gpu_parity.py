@@ -161,6 +161,32 @@ def test_dense_comparator(name):
     assert_bf16_parity(got[:, :, rows], ref, name + " dense (256 rows/head)")
 
 
+# ------------------------------------------------------------------ frame-aligned blocks (r_axes = 2)
+# b2 = H*W = 1560 spatial tokens per stage-R block, b1 = T frames per stage-L group: stage R runs
+# the streaming kernel (25 key tiles per block), stage L the short-group kernel.
+@pytest.mark.timeout(600)
+def test_frame_blocks_chunk():
+    wl = WORKLOADS["chunk"]
+    q, k, v = make_qkv(wl)
+    got, y = run_monarch(q, k, v, _grid(wl), "bf16", 2)
+    ref, yref = oracle.monarch_attention(q, k, v, _grid(wl), r_axes=2, return_y=True)
+    assert_bf16_parity(y, yref, "chunk r_axes=2 stage R (workspace Y)")
+    assert_bf16_parity(got, ref, "chunk r_axes=2")
+
+
+@pytest.mark.timeout(600)
+def test_frame_blocks_full_sampled():
+    wl = WORKLOADS["full"]
+    q, k, v = make_qkv(wl)
+    got, _ = run_monarch(q, k, v, _grid(wl), "bf16", 2)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(46)
+    heads = sorted(rng.choice(wl.heads, size=3, replace=False).tolist())
+    rows = sorted(rng.choice(wl.n_tokens, size=40, replace=False).tolist()) + [0, wl.n_tokens - 1]
+    ref = oracle.monarch_attention_rows(q[:, heads], k[:, heads], v[:, heads], _grid(wl), rows, r_axes=2)
+    assert_bf16_parity(got[:, heads][:, :, rows], ref, "full r_axes=2 (3 heads x %d rows)" % len(rows))
+
+
 # ------------------------------------------------------------------ closed forms at full scale
 @pytest.mark.timeout(600)
 def test_closed_forms_full_scale():
