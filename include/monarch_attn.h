@@ -110,6 +110,33 @@ int ma_stage_l_fwd(const void *q, const void *k, const void *y, void *out,
                    int32_t r_axes, int32_t tile_t, int32_t tile_h,
                    int32_t head_dim, int32_t dtype, struct ihipStream_t *stream);
 
+/* Backward pass (bf16 only). The pages state that the method's kernels run
+ * the forward and the backward pass with FlashAttention-like tiling (it page
+ * "Finetuning e Implementazione Efficiente"; fr page 2.C; zh page on
+ * finetuning and efficient implementation); the gradient itself is the chain
+ * rule of the forward above. Given dO = dL/dout for out = the forward of
+ * (q, k, v) with the same r_axes and tile (tile_t = tile_h = 0: untiled;
+ * otherwise r_axes = 1), writes dq = dL/dq, dk = dL/dk, dv = dL/dv:
+ *   per token set G of a stage, with P = softmax_rows(s Q_G K_G^T):
+ *     dV_G = P^T dO_G,  dS = P * (dO_G V_G^T - D),  D_i = dO_i . O_i,
+ *     dQ_G = s dS K_G,  dK_G = s dS^T Q_G;
+ *   stage L (V := Y, O := out) gives dQ_L, dK_L and dY; stage R (O := Y,
+ *   dO := dY) gives dQ_R, dK_R and dV; dq = dQ_L + dQ_R, dk = dK_L + dK_R.
+ * out must be the forward output (it enters D). The workspace (at least
+ * ma_bwd_workspace_bytes(...) bytes) holds the recomputed Y, dY and per-query
+ * softmax statistics; it must not overlap any tensor argument, and dq, dk, dv
+ * must not overlap each other or the inputs. dtype MA_F32 returns
+ * MA_ERR_UNSUPPORTED; ma_bwd_workspace_bytes then returns 0. */
+size_t ma_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                              int32_t r_axes, int32_t tile_t, int32_t tile_h,
+                              int32_t head_dim, int32_t dtype);
+int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *out,
+                     const void *dout, void *dq, void *dk, void *dv,
+                     void *workspace, size_t workspace_bytes,
+                     int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                     int32_t r_axes, int32_t tile_t, int32_t tile_h,
+                     int32_t head_dim, int32_t dtype, struct ihipStream_t *stream);
+
 /* Static text for a status code (never NULL). */
 const char *ma_status_string(int status);
 

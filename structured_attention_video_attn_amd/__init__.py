@@ -10,9 +10,11 @@ from ._binding import (  # noqa: F401
     MonarchAttnError,
     dense_attn_fwd,
     load_library,
+    ma_bwd_workspace_bytes,
     ma_stage_l_fwd,
     ma_stage_r_fwd,
     ma_workspace_bytes,
+    monarch_attn_bwd,
     monarch_attn_fwd,
     monarch_attn_tiled_fwd,
 )

@@ -35,6 +35,8 @@ SIGNATURES = {
     "dense_attn_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 5 + [_PTR]),
     "ma_stage_r_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 8 + [_PTR]),
     "ma_stage_l_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 10 + [_PTR]),
+    "ma_bwd_workspace_bytes": (_SIZE, [_I32] * 10),
+    "monarch_attn_bwd": (ctypes.c_int, [_PTR] * 9 + [_SIZE] + [_I32] * 10 + [_PTR]),
     "ma_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ma_last_hip_error": (ctypes.c_int, []),
 }
@@ -156,3 +158,21 @@ def ma_stage_l_fwd(q, k, y, out, T, H, W, r_axes=1, tile_t=0, tile_h=0, stream=N
     _call("ma_stage_l_fwd", _ptr(q), _ptr(k), _ptr(y), _ptr(out), B, h, T, H, W, r_axes, tile_t,
           tile_h, d, _dtype_code(q), _stream_ptr(q, stream))
     return out
+
+
+def ma_bwd_workspace_bytes(batch, heads, T, H, W, r_axes=1, tile_t=0, tile_h=0, head_dim=128,
+                           dtype=MA_BF16) -> int:
+    return int(load_library().ma_bwd_workspace_bytes(batch, heads, T, H, W, r_axes, tile_t, tile_h,
+                                                     head_dim, dtype))
+
+
+def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, workspace, T, H, W, r_axes=1, tile_t=0,
+                     tile_h=0, stream=None):
+    """dq, dk, dv of the forward (same r_axes / tile) given dout; bf16 only."""
+    _check(q, k, v, out, dout, dq, dk, dv)
+    B, h, N, d = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("monarch_attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk),
+          _ptr(dv), _ptr(workspace), ws_bytes, B, h, T, H, W, r_axes, tile_t, tile_h, d,
+          _dtype_code(q), _stream_ptr(q, stream))
+    return dq, dk, dv

@@ -15,6 +15,7 @@
 
 #include "../../include/monarch_attn.h"
 #include "attn_bf16.h"
+#include "attn_bwd_bf16.h"
 #include "attn_f32.h"
 #include "validate.h"
 
@@ -204,6 +205,71 @@ int monarch_common(const void *q, const void *k, const void *v, void *out, void 
   return st;
 }
 
+// ---------------------------------------------------------------- backward
+// Rows per backward workgroup tile and waves (every wave issues whole DMA windows).
+template <int D>
+constexpr int bwd_waves() {
+  return TileGeo<D>::NINST % 4 == 0 ? 4 : 2;
+}
+
+int bwd_waves_for(int64_t d) {
+  switch (d) {
+    case 16: return bwd_waves<16>();
+    case 32: return bwd_waves<32>();
+    case 64: return bwd_waves<64>();
+    default: return bwd_waves<128>();
+  }
+}
+
+// Members per group in the (lse, D) rows: the dK/dV pass reads 128-member
+// windows starting at 64t for t up to ceil(len / 64) (the last one is a
+// prefetch past the group), so every window stays inside its group's rows.
+int64_t stats_stride(const GroupAddr &ga) { return ((int64_t)ga.max_len + 63) / 64 * 64 + 128; }
+
+size_t stats_bytes(const Problem &p, const GroupAddr &ga) {
+  return (size_t)(p.batch * p.heads) * (size_t)ga.n_groups * (size_t)stats_stride(ga) * 8u;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the backward: Y and dY (one tensor each), then the (lse, D)
+// rows of stage L and of stage R.
+size_t bwd_workspace_needed(const Problem &p) {
+  if (p.empty) return 0;
+  return 2 * round256(p.tensor_bytes) + round256(stats_bytes(p, stage_l_groups(p))) +
+         round256(stats_bytes(p, stage_r_groups(p)));
+}
+
+template <int D>
+int launch_bwd_d(bool dq_pass, const BwdLaunch &a, uint32_t blocks, hipStream_t s) {
+  constexpr int NW = bwd_waves<D>();
+  if (dq_pass)
+    hipLaunchKernelGGL((bwd_dq_bf16<D, NW>), dim3(blocks), dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW>), dim3(blocks), dim3(NW * 64), 0, s, a);
+  return hip_status(hipGetLastError());
+}
+
+// One backward pass of one stage over the groups `ga`.
+int run_bwd(const Problem &p, const GroupAddr &ga, bool dq_pass, BwdLaunch a, hipStream_t s) {
+  const int nw = bwd_waves_for(p.D);
+  a.head_elems = p.N * p.D;
+  a.ga = ga;
+  a.n_tiles = (ga.max_len + 32 * nw - 1) / (32 * nw);
+  a.stats_stride = (int32_t)stats_stride(ga);
+  a.scale = (float)(1.0 / sqrt((double)p.D));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
+  const uint64_t blocks = (uint64_t)a.n_tiles * (uint64_t)ga.n_groups * (uint64_t)(p.batch * p.heads);
+  if (blocks == 0) return MA_OK;
+  if (blocks > (uint64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
+  switch (p.D) {
+    case 16: return launch_bwd_d<16>(dq_pass, a, (uint32_t)blocks, s);
+    case 32: return launch_bwd_d<32>(dq_pass, a, (uint32_t)blocks, s);
+    case 64: return launch_bwd_d<64>(dq_pass, a, (uint32_t)blocks, s);
+    default: return launch_bwd_d<128>(dq_pass, a, (uint32_t)blocks, s);
+  }
+}
+
 }  // namespace
 }  // namespace ma
 
@@ -281,6 +347,87 @@ int ma_stage_l_fwd(const void *q, const void *k, const void *y, void *out, int32
   st = plan_launch(p, stage_l_groups(p), q, k, y, out, &pl);
   if (st != MA_OK) return st;
   return run_plan(p, pl, stream);
+}
+
+size_t ma_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                              int32_t r_axes, int32_t tile_t, int32_t tile_h, int32_t head_dim,
+                              int32_t dtype) {
+  Problem p;
+  const bool tiled = tile_t != 0 || tile_h != 0;
+  if (resolve_grid(batch, heads, T, H, W, r_axes, tile_t, tile_h, tiled, head_dim, dtype, &p) != MA_OK)
+    return 0;
+  if (dtype != MA_BF16) return 0;
+  return bwd_workspace_needed(p);
+}
+
+int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                     void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                     int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W, int32_t r_axes,
+                     int32_t tile_t, int32_t tile_h, int32_t head_dim, int32_t dtype,
+                     struct ihipStream_t *stream) {
+  Problem p;
+  const bool tiled = tile_t != 0 || tile_h != 0;
+  int st = resolve_grid(batch, heads, T, H, W, r_axes, tile_t, tile_h, tiled, head_dim, dtype, &p);
+  if (st != MA_OK) return st;
+  if (dtype != MA_BF16) return MA_ERR_UNSUPPORTED;
+  if (p.empty) return MA_OK;
+  const void *ins[5] = {q, k, v, out, dout};
+  void *outs[3] = {dq, dk, dv};
+  for (const void *x : ins)
+    if (x == nullptr) return MA_ERR_INVALID_ARG;
+  for (const void *x : outs)
+    if (x == nullptr) return MA_ERR_INVALID_ARG;
+  for (const void *x : ins)
+    if (!aligned16(x)) return MA_ERR_ALIGNMENT;
+  for (const void *x : outs)
+    if (!aligned16(x)) return MA_ERR_ALIGNMENT;
+  const size_t tb = p.tensor_bytes;
+  for (int i = 0; i < 3; ++i) {
+    for (const void *x : ins)
+      if (overlaps(outs[i], x, tb)) return MA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j], tb)) return MA_ERR_INVALID_ARG;
+  }
+  const size_t need = bwd_workspace_needed(p);
+  if (workspace == nullptr || workspace_bytes < need) return MA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MA_ERR_ALIGNMENT;
+  for (const void *x : ins)
+    if (ranges_overlap(workspace, need, x, tb)) return MA_ERR_INVALID_ARG;
+  for (const void *x : outs)
+    if (ranges_overlap(workspace, need, x, tb)) return MA_ERR_INVALID_ARG;
+
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  void *y = ws;
+  void *dy = ws + round256(tb);
+  const GroupAddr gl = stage_l_groups(p), gr = stage_r_groups(p);
+  float *st_l = reinterpret_cast<float *>(ws + 2 * round256(tb));
+  float *st_r = reinterpret_cast<float *>(ws + 2 * round256(tb) + round256(stats_bytes(p, gl)));
+  // Y = stage R of the forward (recomputed)
+  if (p.r_trivial) {
+    st = copy_async(y, v, tb, stream);
+  } else {
+    Plan pr{};
+    st = plan_launch(p, gr, q, k, v, y, &pr);
+    if (st == MA_OK) st = run_plan(p, pr, stream);
+  }
+  if (st != MA_OK) return st;
+  BwdLaunch a{};
+  // stage L: dQ_L (into dq), (lse, D); then dK_L (into dk) and dY
+  a.q = q; a.k = k; a.v = y; a.o = out; a.dout = dout; a.dq = dq; a.stats = st_l; a.accumulate = 0;
+  st = run_bwd(p, gl, true, a, stream);
+  if (st != MA_OK) return st;
+  a = BwdLaunch{};
+  a.q = q; a.k = k; a.v = y; a.dout = dout; a.dk = dk; a.dv = dy; a.stats = st_l; a.accumulate = 0;
+  st = run_bwd(p, gl, false, a, stream);
+  if (st != MA_OK) return st;
+  // stage R, fed dY: dQ_R and dK_R added to dq and dk; dV
+  a = BwdLaunch{};
+  a.q = q; a.k = k; a.v = v; a.o = y; a.dout = dy; a.dq = dq; a.stats = st_r; a.accumulate = 1;
+  st = run_bwd(p, gr, true, a, stream);
+  if (st != MA_OK) return st;
+  a = BwdLaunch{};
+  a.q = q; a.k = k; a.v = v; a.dout = dy; a.dk = dk; a.dv = dv; a.stats = st_r; a.accumulate = 1;
+  return run_bwd(p, gr, false, a, stream);
 }
 
 const char *ma_status_string(int status) {

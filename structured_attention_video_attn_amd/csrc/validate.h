@@ -34,6 +34,13 @@ inline bool overlaps(const void *a, const void *b, size_t bytes) {
   return x < y + bytes && y < x + bytes;
 }
 
+// [a, a + na) and [b, b + nb) intersect.
+inline bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 // Shape checks shared by all Monarch entry points. tiled: tile_t/tile_h must be >= 1.
 inline int resolve_grid(int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
                         int32_t r_axes, int32_t tile_t, int32_t tile_h, bool tiled,

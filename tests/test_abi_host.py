@@ -142,6 +142,41 @@ def test_tiled_and_stage_argument_errors(lib):
     assert d(None, None, None, None, 1, 12, 0, 128, BF16, None) == OK
 
 
+def test_backward_workspace_and_argument_errors(lib):
+    wsb = lib.ma_bwd_workspace_bytes
+    tb = 12 * 32760 * 128 * 2
+    # Y, dY, then (lse, D) per member: stage L groups of 630 (stride 768), stage R groups of 52 (stride 192)
+    stats_l = 12 * 52 * 768 * 8
+    stats_r = 12 * 630 * 192 * 8
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert wsb(1, 12, 21, 30, 52, 1, 0, 0, 128, BF16) == 2 * r256(tb) + r256(stats_l) + r256(stats_r)
+    assert wsb(1, 12, 21, 30, 52, 1, 0, 0, 128, F32) == 0      # backward is bf16 only
+    assert wsb(1, 12, 21, 30, 52, 1, 0, 0, 48, BF16) == 0      # unsupported head_dim
+    assert wsb(0, 12, 21, 30, 52, 1, 0, 0, 128, BF16) == 0     # empty
+    f = lib.monarch_attn_bwd
+    q, k, v, o, do, dq, dk, dv, w = _ptrs(9)
+    nb = wsb(1, 12, 21, 30, 52, 1, 0, 0, 128, BF16)
+
+    def call(q=q, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv, w=w, wb=nb, r=1, tt=0, th=0, d=128, dt=BF16,
+             batch=1):
+        return f(q, k, v, o, do, dq, dk, dv, w, wb, batch, 12, 21, 30, 52, r, tt, th, d, dt, None)
+
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(d=48) == UNSUPPORTED
+    assert call(do=None) == INVALID
+    assert call(dv=None) == INVALID
+    assert call(dk=A16 + 6 * BIG + 4) == ALIGN
+    assert call(dq=q) == INVALID                    # a gradient aliases an input
+    assert call(dv=dk) == INVALID                   # two gradients alias
+    assert call(w=None) == WORKSPACE
+    assert call(wb=nb - 1) == WORKSPACE
+    assert call(w=do) == INVALID                    # workspace aliases dout
+    assert call(w=do + 4096) == INVALID             # workspace starts inside dout
+    assert call(w=A16 + 9 * BIG, k=A16 + 9 * BIG + nb - 16) == INVALID   # k starts inside the workspace
+    assert call(r=2, tt=3, th=30) == INVALID        # tiles need r_axes 1
+    assert call(q=None, k=None, v=None, o=None, do=None, dq=None, dk=None, dv=None, w=None, batch=0) == OK
+
+
 def _parse_groups(text):
     r, l = [], []
     lines = text.strip().splitlines()
