@@ -292,6 +292,17 @@ def main():
         # frame-aligned blocks (r_axes = 2): b2 = H*W = 1560, b1 = T = 21
         ms_frames = time_loop(lambda i: step_r2(i), args.steps, args.warmup)
         ms_dense = time_loop(lambda i: ma.dense_attn_fwd(q, k, v, o), 3, 1)
+        # backward of the headline operator (bf16): dq, dk, dv given dO
+        dout = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                           dtype=torch.float32).to(torch.bfloat16)
+        grads = [torch.empty_like(q) for _ in range(3)]
+        wsb = torch.empty(ma.ma_bwd_workspace_bytes(1, heads, T, H, W, 1, 0, 0, d, ma.MA_BF16) // 2,
+                          dtype=torch.bfloat16, device=dev)
+        ma.monarch_attn_fwd(q, k, v, o, ws, T, H, W)
+        ms_bwd = time_loop(lambda i: ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W),
+                           max(3, args.steps // 4), 2)
+        del grads, wsb, dout
+        bwd_flops = 2.5 * (fr + fl)
         fr3, br3 = stage_work(N, d, heads, W)
         fl3, bl3 = stage_work(N, d, heads, tt * th)
         extras = {
@@ -303,6 +314,11 @@ def main():
             "frame_blocks_roofline_frac": round(
                 (roofline_us(*stage_work(N, d, heads, H * W)) + roofline_us(*stage_work(N, d, heads, T)))
                 / (ms_frames * 1e3), 4),
+            "backward_ms": round(ms_bwd, 4),
+            # algorithmic work of a backward, counted as FlashAttention does: 2.5x the forward's
+            # matmul flops (five products against two); the kernels also recompute Y and P
+            "backward_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 1),
+            "backward_mfma_frac": round(bwd_flops / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "dense_ms": round(ms_dense, 3),
             "dense_tflops": round(4.0 * N * N * d * heads / (ms_dense * 1e-3) / 1e12, 1),
             "monarch_speedup_vs_dense": round(ms_dense / ms, 2),

@@ -99,8 +99,10 @@ def test_backward_chunk(name):
     do = to_bf16_f32(np.random.default_rng(31).standard_normal(q.shape, dtype=np.float32))
     grid = (wl.T, wl.H, wl.W)
     check(run_bwd(q, k, v, do, grid), mb.monarch_attention_backward(q, k, v, do, grid), name + " bwd")
-    check(run_bwd(q, k, v, do, grid, 1, wl.tile), mb.monarch_attention_backward(q, k, v, do, grid, tile=wl.tile),
-          name + " bwd tiled %s" % (wl.tile,))
+    # (3, 10) boxes: three per stage-L group at this 3-frame grid (the workload's own 3 x 30
+    # tile spans whole groups here, where tiled and untiled coincide)
+    check(run_bwd(q, k, v, do, grid, 1, (3, 10)), mb.monarch_attention_backward(q, k, v, do, grid, tile=(3, 10)),
+          name + " bwd tiled (3, 10)")
 
 
 @pytest.mark.timeout(900)
@@ -110,6 +112,16 @@ def test_backward_full_two_heads():
     do = to_bf16_f32(np.random.default_rng(32).standard_normal(q.shape, dtype=np.float32))
     grid = (wl.T, wl.H, wl.W)
     check(run_bwd(q, k, v, do, grid), mb.monarch_attention_backward(q, k, v, do, grid), "full bwd (2 heads)")
+
+
+@pytest.mark.timeout(900)
+def test_backward_structured_tiled_two_heads():
+    wl = WORKLOADS["structured"]
+    q, k, v = make_qkv(wl, heads=2)
+    do = to_bf16_f32(np.random.default_rng(34).standard_normal(q.shape, dtype=np.float32))
+    grid = (wl.T, wl.H, wl.W)
+    check(run_bwd(q, k, v, do, grid, 1, wl.tile), mb.monarch_attention_backward(q, k, v, do, grid, tile=wl.tile),
+          "structured bwd tiled %s (2 heads)" % (wl.tile,))
 
 
 @pytest.mark.timeout(600)
