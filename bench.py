@@ -43,10 +43,10 @@ def parse_args():
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets in the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip tiled/dense side figures")
-    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy"],
+    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy", "backward"],
                     help="run only this kernel (or a plain device copy of one input tensor, the "
-                         "calibration for byte counters) --steps times on the 21x30x52 workload; "
-                         "for counter collection under rocprofv3")
+                         "calibration for byte counters; or the whole backward) --steps times on "
+                         "the 21x30x52 workload; for rocprofv3")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output (kernel runs and "
@@ -179,10 +179,19 @@ def profile_only(which, steps, n_sets=3):
         ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
         sets.append((q, k, v, y, torch.empty_like(q)))
     del base
+    if which == "backward":
+        gen = torch.Generator(device=dev).manual_seed(7)
+        dout = torch.randn(sets[0][0].shape, generator=gen, device=dev).to(torch.bfloat16)
+        grads = [torch.empty_like(dout) for _ in range(3)]
+        wsb = torch.empty(ma.ma_bwd_workspace_bytes(1, 12, T, H, W) // 2, dtype=torch.bfloat16, device=dev)
+        for q, k, v, y, o in sets:
+            ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
     torch.cuda.synchronize()
     for i in range(steps):
         q, k, v, y, o = sets[i % n_sets]
-        if which == "stage_l":
+        if which == "backward":
+            ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W)
+        elif which == "stage_l":
             ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
         elif which == "stage_r":
             ma.ma_stage_r_fwd(q, k, v, y, T, H, W)

@@ -18,6 +18,8 @@
 //                  and dO tiles with their (lse, D): S = Q K^T, dP = dO V^T,
 //                  P = exp2(s log2e S - lse), dS = P*(dP-D);
 //                  dV^T += dO^T P and dK^T += Q^T dS; dK = s dKacc.
+// Groups of at most 64 members instead take bwd_small_bf16: one workgroup per
+// group does both passes' work from one LDS copy of the group.
 // Rows outside the group are clamped duplicates (finite) and get zero weight.
 #pragma once
 #include "attn_bf16.h"
@@ -40,6 +42,48 @@ struct BwdLaunch {
   int32_t accumulate;      // add to dq (dq pass) / dk (dkdv pass) instead of overwriting
   float scale;             // 1/sqrt(D)
   float scale_log2;        // scale * log2(e)
+};
+
+// The 1 KB DMA windows one wave issues per tile (window ii = wave + NW w,
+// w < NINST / NW), rows past the group repeating its last member. One-level
+// groups (member m at token base + m * stride_in) take a per-window offset
+// computed once and one 24-bit multiply-add per window; two-level groups
+// (tiled boxes spanning several outer rows, or offsets of 2^24 bytes or more)
+// take the general row map.
+template <int D, int NW, bool kTwoLevel>
+struct RowWindows {
+  using G = TileGeo<D>;
+  static constexpr int WPT = G::NINST / NW;
+  RowMap rm;
+  uint32_t mstride;    // bytes between consecutive members
+  uint32_t csb[WPT];   // member 0's row offset plus this lane's swizzled chunk, per window
+  int32_t lane_row;
+  int wave, lane;
+
+  __device__ __forceinline__ RowWindows(const GroupGeom &geo, int wave_, int lane_) : wave(wave_), lane(lane_) {
+    rm = row_map(geo);
+    mstride = (uint32_t)rm.stride_in * (2u * D);
+    lane_row = lane / G::CPR;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) {
+      const int slot = (wave + NW * w) * 64 + lane;
+      csb[w] = (uint32_t)rm.base * (2u * D) + 16u * (uint32_t)swizzle_chunk<G::CPR>(slot / G::CPR, slot % G::CPR);
+    }
+  }
+  // window w of the tile holding group rows [k0, k0 + 64)
+  __device__ __forceinline__ void issue(const unsigned char *src, unsigned char *tile, int32_t k0, int w) const {
+    const int ii = wave + NW * w;
+    if constexpr (kTwoLevel) {
+      dma_row_window<D>(src, tile, rm, k0, ii, lane);
+    } else {
+      const int32_t km = min(lane_row + (k0 + ii * G::ROWS_PER_INST), rm.last);
+      dma16(src, __umul24((uint32_t)km, mstride) + csb[w], tile + ii * 1024);
+    }
+  }
+  __device__ __forceinline__ void tile(const unsigned char *src, unsigned char *dst, int32_t k0) const {
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) issue(src, dst, k0, w);
+  }
 };
 
 // c0 / c1 (rows 0..31 / 32..63 of a 64-row LDS tile, 32 columns of this
@@ -175,12 +219,13 @@ __device__ __forceinline__ void store_rows_lds(unsigned char *ot, const f32x16_t
 }
 
 // ---------------------------------------------------------------------------
-// dQ pass. Ring: keys in LDS tiles 0..2 (tile t in t % 3), values in 3..4.
+// dQ pass (two workgroups per CU: 80 KB of LDS and at most 256 registers).
+// Ring: keys in LDS tiles 0..2 (tile t in t % 3), values in 3..4.
 // Step t issues the value windows of tile t+1, then the key windows of tile
 // t+2 (rows past the group clamped), so the wait opening step t+1 may leave
 // the newest WPT windows in flight.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16(BwdLaunch p) {
+template <int D, int NW, bool kTwoLevel>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16(BwdLaunch p) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
   constexpr int WPT = G::NINST / NW;
@@ -196,7 +241,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16(BwdLaunch p) {
   const int32_t qbase = qt * 32 * NW;
   if (qbase >= geo.len) return;   // uniform
   const int32_t qend = min(geo.len, qbase + 32 * NW);
-  const RowMap rm = row_map(geo);
   const int64_t slice = bh * p.head_elems;
   const unsigned char *kbytes = uniform_ptr(reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + slice));
   const unsigned char *vbytes = uniform_ptr(reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.v) + slice));
@@ -210,14 +254,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16(BwdLaunch p) {
   const int32_t q0 = qbase + wave * 32, qm = q0 + col;
   const bool wave_active = q0 < qend;
 
+  const RowWindows<D, NW, kTwoLevel> win(geo, wave, lane);
   const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
   // prologue: K(0), V(0), K(1), then this lane's query, dO and O rows
-#pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, lds, rm, 0, wave + NW * w, lane);
-#pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(vbytes, lds + 3 * G::TILEB, rm, 0, wave + NW * w, lane);
-#pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, lds + G::TILEB, rm, kKeyTile, wave + NW * w, lane);
+  win.tile(kbytes, lds, 0);
+  win.tile(vbytes, lds + 3 * G::TILEB, 0);
+  win.tile(kbytes, lds + G::TILEB, kKeyTile);
   bf16x8_t qb[DK], db[DK], ob[DK];
   load_row_frags<D>(static_cast<const u16 *>(p.q) + slice, geo, qm, half, qb);
   load_row_frags<D>(static_cast<const u16 *>(p.dout) + slice, geo, qm, half, db);
@@ -243,10 +285,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16(BwdLaunch p) {
     const unsigned char *vc = lds + (3 + ys) * G::TILEB;
     unsigned char *vn = lds + (3 + (ys ^ 1)) * G::TILEB;
     unsigned char *kn = lds + (ks == 0 ? 2 : ks - 1) * G::TILEB;
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) dma_row_window<D>(vbytes, vn, rm, (t + 1) * kKeyTile, wave + NW * w, lane);
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) dma_row_window<D>(kbytes, kn, rm, (t + 2) * kKeyTile, wave + NW * w, lane);
+    win.tile(vbytes, vn, (t + 1) * kKeyTile);
+    win.tile(kbytes, kn, (t + 2) * kKeyTile);
     if (wave_active) {
       f32x16_t s0, s1, t0, t1;
       tile_times<D>(kc, qb, lo, s0, s1);   // S^T: rows = keys
@@ -305,17 +345,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16(BwdLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV pass. Ring: query tiles in LDS tiles 0..2, dO tiles in 3..4, and the
-// (lse, D) window of each dO tile (128 members x 8 bytes, of which the tile
-// uses 64) in two 1 KB slots. Step t issues dO(t+1), stats(t+1), then Q(t+2).
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16(BwdLaunch p) {
+// dK/dV pass. Double buffers: query tiles in LDS tiles 0..1, dO tiles in
+// 2..3, and the (lse, D) window of each dO tile (128 members x 8 bytes, of
+// which the tile uses 64) in two 1 KB slots; step t issues dO, stats and Q of
+// tile t+1. At head_dim 128 its live registers (dK^T and dV^T accumulators,
+// this wave's key and value rows, S and dP of a tile) exceed the 256 that two
+// waves per SIMD allow, and spilling costs more than the lost occupancy, so
+// it runs one wave per SIMD there; smaller head dims fit two.
+template <int D, int NW, bool kTwoLevel>
+__global__ __launch_bounds__(NW * 64, D >= 128 ? 1 : 2) void bwd_dkdv_bf16(BwdLaunch p) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
-  constexpr int WPT = G::NINST / NW;
   constexpr int DK = G::DK, DB = G::DB;
-  __shared__ __align__(1024) unsigned char lds[5 * G::TILEB + 2048];
-  unsigned char *const st_lds = lds + 5 * G::TILEB;
+  __shared__ __align__(1024) unsigned char lds[4 * G::TILEB + 2048];
+  unsigned char *const st_lds = lds + 4 * G::TILEB;
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t kt = (int32_t)(bid % (uint32_t)p.n_tiles);
@@ -326,7 +369,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16(BwdLaunch p) {
   const int32_t kbase = kt * 32 * NW;
   if (kbase >= geo.len) return;   // uniform
   const int32_t kend = min(geo.len, kbase + 32 * NW);
-  const RowMap rm = row_map(geo);
   const int64_t slice = bh * p.head_elems;
   const unsigned char *qbytes = uniform_ptr(reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.q) + slice));
   const unsigned char *dbytes = uniform_ptr(reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.dout) + slice));
@@ -342,18 +384,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16(BwdLaunch p) {
   const int32_t k0w = kbase + wave * 32, km = k0w + col;
   const bool wave_active = k0w < kend;
 
+  const RowWindows<D, NW, kTwoLevel> win(geo, wave, lane);
   const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
   auto stats_window = [&](int32_t t, int slot) __attribute__((always_inline)) {
     // members [64t, 64t + 128): 1 KB, 16 bytes per lane; every wave issues the same window
     dma16(sbytes, (uint32_t)(t * kKeyTile * 8 + 16 * lane), st_lds + slot * 1024);
   };
-#pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(qbytes, lds, rm, 0, wave + NW * w, lane);
-#pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(dbytes, lds + 3 * G::TILEB, rm, 0, wave + NW * w, lane);
+  win.tile(qbytes, lds, 0);
+  win.tile(dbytes, lds + 2 * G::TILEB, 0);
   stats_window(0, 0);
-#pragma unroll
-  for (int w = 0; w < WPT; ++w) dma_row_window<D>(qbytes, lds + G::TILEB, rm, kKeyTile, wave + NW * w, lane);
   bf16x8_t kb[DK], vb[DK];
   load_row_frags<D>(static_cast<const u16 *>(p.k) + slice, geo, km, half, kb);
   load_row_frags<D>(static_cast<const u16 *>(p.v) + slice, geo, km, half, vb);
@@ -365,20 +404,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16(BwdLaunch p) {
   f32x16_t dka[DB], dva[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) dka[b] = dva[b] = f32x16_t{};
-  int qs = 0, ds = 0;
   for (int32_t t = 0; t < n; ++t) {
-    if (t > 0) wait_vmcnt<WPT>();   // leave the query windows of tile t+1 in flight
-    __syncthreads();
-    const unsigned char *qc = lds + qs * G::TILEB;
-    const unsigned char *dc = lds + (3 + ds) * G::TILEB;
-    const unsigned char *sc = st_lds + ds * 1024;
-    unsigned char *dn = lds + (3 + (ds ^ 1)) * G::TILEB;
-    unsigned char *qn = lds + (qs == 0 ? 2 : qs - 1) * G::TILEB;
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) dma_row_window<D>(dbytes, dn, rm, (t + 1) * kKeyTile, wave + NW * w, lane);
-    stats_window(t + 1, ds ^ 1);
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) dma_row_window<D>(qbytes, qn, rm, (t + 2) * kKeyTile, wave + NW * w, lane);
+    if (t > 0) wait_vmcnt<0>();   // tile t: the only DMAs in flight
+    __syncthreads();              // ... landed for every wave, and tile t-1's buffers are free
+    const int cur = t & 1;
+    const unsigned char *qc = lds + cur * G::TILEB;
+    const unsigned char *dc = lds + (2 + cur) * G::TILEB;
+    const unsigned char *sc = st_lds + cur * 1024;
+    win.tile(dbytes, lds + (3 - cur) * G::TILEB, (t + 1) * kKeyTile);
+    stats_window(t + 1, cur ^ 1);
+    win.tile(qbytes, lds + (1 - cur) * G::TILEB, (t + 1) * kKeyTile);
     if (wave_active) {
       f32x16_t s0, s1, t0, t1;
       tile_times<D>(qc, kb, lo, s0, s1);   // S: rows = queries of the tile, columns = this wave's keys
@@ -424,8 +459,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16(BwdLaunch p) {
       tile_t_times<D>(dc, p0, p1, lo, tr_col, dva);   // dV^T += dO^T P
       tile_t_times<D>(qc, g0, g1, lo, tr_col, dka);   // dK^T += Q^T dS
     }
-    qs = qs == 2 ? 0 : qs + 1;
-    ds ^= 1;
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -435,6 +468,150 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_bf16(BwdLaunch p) {
                     p.accumulate != 0);
   __syncthreads();
   store_rows_lds<D>(ot, dva, 1.f, col, half, lane, static_cast<u16 *>(p.dv) + slice, geo, k0w, kend, false);
+}
+
+// ---------------------------------------------------------------------------
+// Groups of at most 64 members: the whole backward of one group in one
+// workgroup, from one LDS copy of its Q, K, V and dO tiles (rows past the
+// group repeat its last member). Waves 0-1 own queries 32w..32w+31: S^T and
+// dP^T against the key and value tiles, the row softmax, D = sum_k P dP (the
+// whole row is on chip, so dO . O is not needed), (lse, D) into LDS, then
+// dQ^T = K^T dS^T. Waves 2-3 own keys 32w..32w+31: S and dP against the
+// query and dO tiles while the query waves finish the softmax, then, with
+// (lse, D) from LDS, P, dS, dV^T = dO^T P and dK^T = Q^T dS.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_small_bf16(BwdLaunch p) {
+  using G = TileGeo<D>;
+  constexpr int DK = G::DK, DB = G::DB;
+  __shared__ __align__(1024) unsigned char lds[4 * G::TILEB + 64 * 8];
+  unsigned char *const qt = lds, *const kt = lds + G::TILEB, *const vt = lds + 2 * G::TILEB,
+                       *const dt = lds + 3 * G::TILEB;
+  unsigned char *const stl = lds + 4 * G::TILEB;   // (lse, D) per member, float2
+
+  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int32_t g = (int32_t)(bid % (uint32_t)p.ga.n_groups);
+  const int64_t bh = (int64_t)(bid / (uint32_t)p.ga.n_groups);
+  const GroupGeom geo = group_geom(p.ga, g);
+  if (geo.len <= 0) return;   // uniform
+  const RowMap rm = row_map(geo);
+  const int64_t slice = bh * p.head_elems;
+  const void *const srcs[4] = {p.q, p.k, p.v, p.dout};
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int tr_key = 4 * half + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const LaneOffsets<D> lo = lane_offsets<D>(col, half, tr_key, tr_col);
+
+#pragma unroll
+  for (int tile = 0; tile < 4; ++tile) {
+    const unsigned char *src =
+        uniform_ptr(reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(srcs[tile]) + slice));
+    for (int ii = wave; ii < G::NINST; ii += 4) dma_row_window<D>(src, lds + tile * G::TILEB, rm, 0, ii, lane);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const bool qrole = wave < 2;
+  const int w2 = wave & 1;
+  // this lane's own row (a query or a key) of the two register operands, read from its tile
+  const unsigned char *own_a = (qrole ? qt : kt) + 32 * w2 * G::ROWB;
+  const unsigned char *own_b = (qrole ? dt : vt) + 32 * w2 * G::ROWB;
+  bf16x8_t fa[DK], fb[DK];
+#pragma unroll
+  for (int j = 0; j < DK; ++j) {
+    fa[j] = *reinterpret_cast<const bf16x8_t *>(own_a + lo.k[j]);
+    fb[j] = *reinterpret_cast<const bf16x8_t *>(own_b + lo.k[j]);
+  }
+  // query waves: S^T = K Q^T, dP^T = V dO^T; key waves: S = Q K^T, dP = dO V^T
+  f32x16_t s0, s1, t0, t1;
+  tile_times<D>(qrole ? kt : qt, fa, lo, s0, s1);
+  tile_times<D>(qrole ? vt : dt, fb, lo, t0, t1);
+
+  bf16x8_t w0[2], w1[2];   // query waves: dS^T (rows = keys)
+  if (qrole) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t key = 8 * (r / 4) + 4 * half + (r % 4);
+      if (key >= geo.len) s0[r] = -INFINITY;
+      if (key + 32 >= geo.len) s1[r] = -INFINITY;
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m = mx * p.scale_log2;
+    float l = 0.f, u = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_log2, -m));
+      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_log2, -m));
+      l += s0[r] + s1[r];
+      u = fmaf(s0[r], t0[r], fmaf(s1[r], t1[r], u));
+    }
+    l += swap_halves(l);
+    u += swap_halves(u);
+    const float inv_l = 1.f / l;
+    const float dq_row = u * inv_l;   // D = sum_k P dP of this query
+    if (half == 0) {
+      float2 *st = reinterpret_cast<float2 *>(stl) + 32 * w2 + col;
+      *st = make_float2(m + __builtin_log2f(l), dq_row);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      pack_pair(s0[r] * inv_l * (t0[r] - dq_row), s0[r + 1] * inv_l * (t0[r + 1] - dq_row), r, w0);
+      pack_pair(s1[r] * inv_l * (t1[r] - dq_row), s1[r + 1] * inv_l * (t1[r + 1] - dq_row), r, w1);
+    }
+  }
+  __syncthreads();   // (lse, D) of every query in LDS
+
+  f32x16_t acc_a[DB], acc_b[DB];   // query waves: dQ^T in acc_a; key waves: dK^T in acc_a, dV^T in acc_b
+#pragma unroll
+  for (int b = 0; b < DB; ++b) acc_a[b] = acc_b[b] = f32x16_t{};
+  if (qrole) {
+    tile_t_times<D>(kt, w0, w1, lo, tr_col, acc_a);
+  } else {
+    bf16x8_t p0[2], p1[2], g0[2], g1[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int row = 32 * blk + 8 * r4 + 4 * half;   // queries row .. row+3
+        const f32x4_t st01 = *reinterpret_cast<const f32x4_t *>(stl + row * 8);
+        const f32x4_t st23 = *reinterpret_cast<const f32x4_t *>(stl + row * 8 + 16);
+        const float lse[4] = {st01[0], st01[2], st23[0], st23[2]};
+        const float dd[4] = {st01[1], st01[3], st23[1], st23[3]};
+        float pv[4], gv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float sv = blk ? s1[r] : s0[r];
+          const float tv = blk ? t1[r] : t0[r];
+          const bool valid = row + e < geo.len;   // repeated rows past the group get zero weight
+          const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sv, p.scale_log2, -lse[e])) : 0.f;
+          pv[e] = pr;
+          gv[e] = pr * (tv - dd[e]);
+        }
+        bf16x8_t(&pp)[2] = blk ? p1 : p0;
+        bf16x8_t(&gg)[2] = blk ? g1 : g0;
+        pack_pair(pv[0], pv[1], 4 * r4, pp);
+        pack_pair(pv[2], pv[3], 4 * r4 + 2, pp);
+        pack_pair(gv[0], gv[1], 4 * r4, gg);
+        pack_pair(gv[2], gv[3], 4 * r4 + 2, gg);
+      }
+    }
+    tile_t_times<D>(dt, p0, p1, lo, tr_col, acc_b);   // dV^T += dO^T P
+    tile_t_times<D>(qt, g0, g1, lo, tr_col, acc_a);   // dK^T += Q^T dS
+  }
+  __syncthreads();   // every tile read: the waves' 32-row fp32 staging areas may reuse them
+  unsigned char *ot = lds + wave * 32 * (4 * D);
+  const int32_t r0 = 32 * w2;
+  store_rows_lds<D>(ot, acc_a, p.scale, col, half, lane,
+                    static_cast<u16 *>(qrole ? p.dq : p.dk) + slice, geo, r0, geo.len, p.accumulate != 0);
+  __syncthreads();
+  if (!qrole)
+    store_rows_lds<D>(ot, acc_b, 1.f, col, half, lane, static_cast<u16 *>(p.dv) + slice, geo, r0, geo.len, false);
 }
 
 }  // namespace ma

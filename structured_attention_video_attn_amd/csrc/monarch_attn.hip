@@ -101,6 +101,15 @@ int launch_d(const Plan &pl, hipStream_t s) {
   return hip_status(hipGetLastError());
 }
 
+// The streaming kernels' DMA addressing: two-level when some group spans
+// several outer rows (tiled boxes), or when member offsets do not fit the
+// 24-bit multiply of the one-level form.
+bool two_level(const Problem &p, const GroupAddr &ga) {
+  const bool outer = ga.len_o > 1 && ga.tile_o > 1;
+  const int64_t mstride = (int64_t)ga.stride_in * 2 * p.D;
+  return outer || ga.max_len >= (1 << 24) || mstride >= (1 << 24);
+}
+
 int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void *k,
                 const void *vals, void *out, Plan *pl) {
   AttnLaunch a{};
@@ -138,9 +147,7 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
     pl->waves = w;
     q_per_block = (int)(kQueriesPerWave * need);
     pl->kernel = Kernel::kStream;
-    const bool outer = ga.len_o > 1 && ga.tile_o > 1;
-    const int64_t mstride = (int64_t)ga.stride_in * 2 * p.D;
-    pl->two_level = outer || ga.max_len >= (1 << 24) || mstride >= (1 << 24);
+    pl->two_level = two_level(p, ga);
   }
   a.n_qtiles = (ga.max_len + q_per_block - 1) / q_per_block;
   a.q_tile = q_per_block;
@@ -241,12 +248,39 @@ size_t bwd_workspace_needed(const Problem &p) {
 }
 
 template <int D>
-int launch_bwd_d(bool dq_pass, const BwdLaunch &a, uint32_t blocks, hipStream_t s) {
+int launch_bwd_d(bool dq_pass, bool two_level, const BwdLaunch &a, uint32_t blocks, hipStream_t s) {
   constexpr int NW = bwd_waves<D>();
-  if (dq_pass)
-    hipLaunchKernelGGL((bwd_dq_bf16<D, NW>), dim3(blocks), dim3(NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW>), dim3(blocks), dim3(NW * 64), 0, s, a);
+  const dim3 grid(blocks), block(NW * 64);
+  if (dq_pass) {
+    if (two_level)
+      hipLaunchKernelGGL((bwd_dq_bf16<D, NW, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16<D, NW, false>), grid, block, 0, s, a);
+  } else {
+    if (two_level)
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, false>), grid, block, 0, s, a);
+  }
+  return hip_status(hipGetLastError());
+}
+
+// Whole backward of one stage whose groups have at most 64 members.
+int run_bwd_small(const Problem &p, const GroupAddr &ga, BwdLaunch a, hipStream_t s) {
+  a.head_elems = p.N * p.D;
+  a.ga = ga;
+  a.scale = (float)(1.0 / sqrt((double)p.D));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
+  const uint64_t blocks = (uint64_t)ga.n_groups * (uint64_t)(p.batch * p.heads);
+  if (blocks == 0) return MA_OK;
+  if (blocks > (uint64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
+  const dim3 grid((uint32_t)blocks), block(256);
+  switch (p.D) {
+    case 16: hipLaunchKernelGGL((bwd_small_bf16<16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((bwd_small_bf16<32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((bwd_small_bf16<64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((bwd_small_bf16<128>), grid, block, 0, s, a); break;
+  }
   return hip_status(hipGetLastError());
 }
 
@@ -262,12 +296,30 @@ int run_bwd(const Problem &p, const GroupAddr &ga, bool dq_pass, BwdLaunch a, hi
   const uint64_t blocks = (uint64_t)a.n_tiles * (uint64_t)ga.n_groups * (uint64_t)(p.batch * p.heads);
   if (blocks == 0) return MA_OK;
   if (blocks > (uint64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
+  const bool tl = two_level(p, ga);
   switch (p.D) {
-    case 16: return launch_bwd_d<16>(dq_pass, a, (uint32_t)blocks, s);
-    case 32: return launch_bwd_d<32>(dq_pass, a, (uint32_t)blocks, s);
-    case 64: return launch_bwd_d<64>(dq_pass, a, (uint32_t)blocks, s);
-    default: return launch_bwd_d<128>(dq_pass, a, (uint32_t)blocks, s);
+    case 16: return launch_bwd_d<16>(dq_pass, tl, a, (uint32_t)blocks, s);
+    case 32: return launch_bwd_d<32>(dq_pass, tl, a, (uint32_t)blocks, s);
+    case 64: return launch_bwd_d<64>(dq_pass, tl, a, (uint32_t)blocks, s);
+    default: return launch_bwd_d<128>(dq_pass, tl, a, (uint32_t)blocks, s);
   }
+}
+
+// Backward of one stage: dq (+)= dQ, dk (+)= dK (accumulate), dv = dV, for the
+// stage O_s = softmax-attention(q, k, v) over the groups `ga`, given the
+// stage's output `o` and its gradient `dout`; `stats` holds the (lse, D) rows
+// of the two-pass form.
+int run_stage_bwd(const Problem &p, const GroupAddr &ga, const void *q, const void *k, const void *v,
+                  const void *o, const void *dout, void *dq, void *dk, void *dv, float *stats, bool accumulate,
+                  hipStream_t s) {
+  BwdLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.accumulate = accumulate ? 1 : 0;
+  if (ga.max_len <= kKeyTile) return run_bwd_small(p, ga, a, s);
+  a.o = o; a.stats = stats;
+  int st = run_bwd(p, ga, true, a, s);
+  if (st != MA_OK) return st;
+  return run_bwd(p, ga, false, a, s);
 }
 
 }  // namespace
@@ -402,32 +454,25 @@ int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *ou
   const GroupAddr gl = stage_l_groups(p), gr = stage_r_groups(p);
   float *st_l = reinterpret_cast<float *>(ws + 2 * round256(tb));
   float *st_r = reinterpret_cast<float *>(ws + 2 * round256(tb) + round256(stats_bytes(p, gl)));
-  // Y = stage R of the forward (recomputed)
-  if (p.r_trivial) {
-    st = copy_async(y, v, tb, stream);
-  } else {
+  if (p.l_trivial && !p.r_trivial) {
+    // stage L is the identity: O = Y and dY = dO, and stage R alone writes dq and dk
+    return run_stage_bwd(p, gr, q, k, v, out, dout, dq, dk, dv, st_r, false, stream);
+  }
+  // Y = stage R of the forward, recomputed (V itself when stage R is the identity)
+  const void *yv = v;
+  if (!p.r_trivial) {
     Plan pr{};
     st = plan_launch(p, gr, q, k, v, y, &pr);
     if (st == MA_OK) st = run_plan(p, pr, stream);
+    if (st != MA_OK) return st;
+    yv = y;
   }
-  if (st != MA_OK) return st;
-  BwdLaunch a{};
-  // stage L: dQ_L (into dq), (lse, D); then dK_L (into dk) and dY
-  a.q = q; a.k = k; a.v = y; a.o = out; a.dout = dout; a.dq = dq; a.stats = st_l; a.accumulate = 0;
-  st = run_bwd(p, gl, true, a, stream);
-  if (st != MA_OK) return st;
-  a = BwdLaunch{};
-  a.q = q; a.k = k; a.v = y; a.dout = dout; a.dk = dk; a.dv = dy; a.stats = st_l; a.accumulate = 0;
-  st = run_bwd(p, gl, false, a, stream);
-  if (st != MA_OK) return st;
+  // stage L: dQ_L into dq, dK_L into dk, and dY (which is dV itself when stage R
+  // is the identity: its single-member groups add nothing to dq and dk)
+  st = run_stage_bwd(p, gl, q, k, yv, out, dout, dq, dk, p.r_trivial ? dv : dy, st_l, false, stream);
+  if (st != MA_OK || p.r_trivial) return st;
   // stage R, fed dY: dQ_R and dK_R added to dq and dk; dV
-  a = BwdLaunch{};
-  a.q = q; a.k = k; a.v = v; a.o = y; a.dout = dy; a.dq = dq; a.stats = st_r; a.accumulate = 1;
-  st = run_bwd(p, gr, true, a, stream);
-  if (st != MA_OK) return st;
-  a = BwdLaunch{};
-  a.q = q; a.k = k; a.v = v; a.dout = dy; a.dk = dk; a.dv = dv; a.stats = st_r; a.accumulate = 1;
-  return run_bwd(p, gr, false, a, stream);
+  return run_stage_bwd(p, gr, q, k, v, y, dy, dq, dk, dv, st_r, true, stream);
 }
 
 const char *ma_status_string(int status) {
