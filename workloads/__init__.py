@@ -19,6 +19,11 @@ Workloads (grid, heads, head_dim, storage dtype, value recipe):
 
 The 30x52 per-frame grid stands in for the 480p latent grid of the video
 models the MonarchRT pages evaluate on; the pages never print their token grid.
+
+The chunk-causal (autoregressive) workload uses the ``full`` inputs with chunks
+of ``CAUSAL_CHUNK_T`` frames: the ``chunk`` shape (3 frames) is one generation
+step's query chunk, and the step with a cache is the last chunk, frames 18..20,
+attending to all 21 frames.
 """
 from __future__ import annotations
 
@@ -28,7 +33,9 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "to_bf16_f32"]
+__all__ = ["Workload", "WORKLOADS", "CAUSAL_CHUNK_T", "make_qkv", "to_bf16_f32"]
+
+CAUSAL_CHUNK_T = 3   # frames per autoregressive chunk
 
 
 @dataclasses.dataclass(frozen=True)
