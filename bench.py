@@ -216,7 +216,7 @@ def main():
     import numpy as np
     import torch
     import structured_attention_video_attn_amd as ma
-    from workloads import WORKLOADS, make_qkv
+    from workloads import CAUSAL_CHUNK_T, WORKLOADS, make_qkv
 
     ma.load_library()   # raises when the HIP library is not built
     dev = torch.device("cuda:0")
@@ -301,6 +301,27 @@ def main():
         # frame-aligned blocks (r_axes = 2): b2 = H*W = 1560, b1 = T = 21
         ms_frames = time_loop(lambda i: step_r2(i), args.steps, args.warmup)
         ms_dense = time_loop(lambda i: ma.dense_attn_fwd(q, k, v, o), 3, 1)
+        # chunk-causal forms (3-frame chunks): the whole sequence, and the last
+        # chunk as one generation step over a cache of Y for frames 0..17
+        ct = CAUSAL_CHUNK_T
+        def causal(i):
+            q_, k_, v_, o_, ws_ = sets[i % len(sets)]
+            ma.monarch_attn_causal_fwd(q_, k_, v_, o_, ws_, T, H, W, ct)
+        ms_causal = time_loop(causal, args.steps, args.warmup)
+        t0 = T - ct
+
+        def chunk_step(i):
+            q_, k_, v_, o_, ws_ = sets[i % len(sets)]
+            ma.monarch_attn_chunk_fwd(q_, k_, v_, ws_.view(q_.shape), o_, T, H, W, t0, ct)
+        ms_step = time_loop(chunk_step, args.steps, args.warmup)
+        fsz = H * W
+        nq = ct * fsz                     # tokens of the chunk
+        causal_l_flops = sum(4.0 * d * heads * W * (ct * H) * ((c + 1) * ct * H) for c in range(T // ct))
+        roof_causal = roofline_us(*stage_work(N, d, heads, W)) + roofline_us(causal_l_flops, 8.0 * N * d * heads)
+        step_bytes_r = 8.0 * nq * d * heads
+        step_bytes_l = 2.0 * d * heads * (2 * nq + 2 * N)   # read Q (chunk), K and Y (all); write O (chunk)
+        step_flops_l = 4.0 * d * heads * W * (ct * H) * (T * H)
+        roof_step = roofline_us(4.0 * nq * d * heads * W, step_bytes_r) + roofline_us(step_flops_l, step_bytes_l)
         # backward of the headline operator (bf16): dq, dk, dv given dO
         dout = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
                            dtype=torch.float32).to(torch.bfloat16)
@@ -323,6 +344,10 @@ def main():
             "frame_blocks_roofline_frac": round(
                 (roofline_us(*stage_work(N, d, heads, H * W)) + roofline_us(*stage_work(N, d, heads, T)))
                 / (ms_frames * 1e3), 4),
+            "causal_chunk3_ms": round(ms_causal, 4),
+            "causal_chunk3_roofline_frac": round(roof_causal / (ms_causal * 1e3), 4),
+            "chunk_step_t18_ms": round(ms_step, 4),
+            "chunk_step_t18_roofline_frac": round(roof_step / (ms_step * 1e3), 4),
             "backward_ms": round(ms_bwd, 4),
             # algorithmic work of a backward, counted as FlashAttention does: 2.5x the forward's
             # matmul flops (five products against two); the kernels also recompute Y and P

@@ -88,6 +88,44 @@ int monarch_attn_tiled_fwd(const void *q, const void *k, const void *v, void *ou
                            int32_t tile_t, int32_t tile_h, int32_t head_dim, int32_t dtype,
                            struct ihipStream_t *stream);
 
+/* Chunk-causal Monarch attention over the whole sequence (bf16 only).
+ * The pages' real-time target is autoregressive generation a few frames at a
+ * time (it 1 and 3; fr 1 and 4; zh 1); they do not define Monarch over a causal
+ * sequence. Reading: frames form chunks of chunk_t (chunk(t) = t div chunk_t);
+ * stage R is as in monarch_attn_fwd (its blocks never cross a frame); in
+ * stage L a query of chunk c uses only the members of its group in chunks
+ * 0..c (bidirectional inside a chunk). The rows of chunk c therefore equal
+ * monarch_attn_fwd over frames [0, (c+1) chunk_t). r_axes must be 0, 1 or 2
+ * (at 3 the single stage-R block would cross frames): MA_ERR_INVALID_ARG
+ * otherwise, or for chunk_t < 1. chunk_t >= T is the bidirectional operator.
+ * Workspace, layout and overlap rules as monarch_attn_fwd; MA_ERR_UNSUPPORTED
+ * for MA_F32. */
+int monarch_attn_causal_fwd(const void *q, const void *k, const void *v, void *out,
+                            void *workspace, size_t workspace_bytes,
+                            int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                            int32_t r_axes, int32_t chunk_t, int32_t head_dim, int32_t dtype,
+                            struct ihipStream_t *stream);
+
+/* One autoregressive step with a cache (bf16 only), under the reading above:
+ * the chunk of frames [t0, t0 + chunk_t) attends to every frame up to its own
+ * end. q, k, v, y and out are whole buffers [batch, heads, T*H*W, head_dim]
+ * for T allocated frames (t0 + chunk_t <= T); only frames below t0 + chunk_t
+ * are read.
+ *   y   in:  frames [0, t0) hold the stage-R output Y of earlier steps (the
+ *            cache); out: frames [t0, t0 + chunk_t) receive this chunk's Y.
+ *            Not used (may be NULL) at r_axes = 0, where Y is V.
+ *   out frames [t0, t0 + chunk_t) receive O; other frames are not written.
+ * Stage R runs over the chunk's frames only; stage L over the members of each
+ * group in frames [0, t0 + chunk_t), with queries in the chunk. Calling it
+ * for t0 = 0, chunk_t, 2 chunk_t, ... reproduces monarch_attn_causal_fwd.
+ * y and out must not overlap each other or q, k, v. MA_ERR_INVALID_ARG for
+ * r_axes = 3, chunk_t < 1, t0 < 0 or t0 + chunk_t > T; MA_ERR_UNSUPPORTED for
+ * MA_F32. No workspace. */
+int monarch_attn_chunk_fwd(const void *q, const void *k, const void *v, void *y, void *out,
+                           int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                           int32_t r_axes, int32_t t0, int32_t chunk_t, int32_t head_dim,
+                           int32_t dtype, struct ihipStream_t *stream);
+
 /* Dense comparator: O = softmax(s Q K^T) V over all n_tokens, per (batch, head)
  * (the quadratic 3D self-attention the method replaces: it page 1, zh overview).
  * out must not overlap q, k, v. */

@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     ma_stage_r_fwd,
     ma_workspace_bytes,
     monarch_attn_bwd,
+    monarch_attn_causal_fwd,
+    monarch_attn_chunk_fwd,
     monarch_attn_fwd,
     monarch_attn_tiled_fwd,
 )

@@ -32,6 +32,8 @@ SIGNATURES = {
     "ma_workspace_bytes": (_SIZE, [_I32] * 10),
     "monarch_attn_fwd": (ctypes.c_int, [_PTR] * 5 + [_SIZE] + [_I32] * 8 + [_PTR]),
     "monarch_attn_tiled_fwd": (ctypes.c_int, [_PTR] * 5 + [_SIZE] + [_I32] * 9 + [_PTR]),
+    "monarch_attn_causal_fwd": (ctypes.c_int, [_PTR] * 5 + [_SIZE] + [_I32] * 9 + [_PTR]),
+    "monarch_attn_chunk_fwd": (ctypes.c_int, [_PTR] * 5 + [_I32] * 10 + [_PTR]),
     "dense_attn_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 5 + [_PTR]),
     "ma_stage_r_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 8 + [_PTR]),
     "ma_stage_l_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 10 + [_PTR]),
@@ -133,6 +135,28 @@ def monarch_attn_tiled_fwd(q, k, v, out, workspace, T, H, W, tile_t, tile_h, str
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("monarch_attn_tiled_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
           ws_bytes, B, h, T, H, W, tile_t, tile_h, d, _dtype_code(q), _stream_ptr(q, stream))
+    return out
+
+
+def monarch_attn_causal_fwd(q, k, v, out, workspace, T, H, W, chunk_t, r_axes=1, stream=None):
+    """Chunk-causal Monarch over the whole sequence (bf16): chunks of chunk_t frames."""
+    _check(q, k, v, out)
+    B, h, N, d = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("monarch_attn_causal_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace), ws_bytes,
+          B, h, T, H, W, r_axes, chunk_t, d, _dtype_code(q), _stream_ptr(q, stream))
+    return out
+
+
+def monarch_attn_chunk_fwd(q, k, v, y, out, T, H, W, t0, chunk_t, r_axes=1, stream=None):
+    """One step with a cache (bf16): frames [t0, t0 + chunk_t) of y and out are written."""
+    if y is None:
+        _check(q, k, v, out)
+    else:
+        _check(q, k, v, out, y)
+    B, h, N, d = q.shape
+    _call("monarch_attn_chunk_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(out), B, h, T, H, W, r_axes,
+          t0, chunk_t, d, _dtype_code(q), _stream_ptr(q, stream))
     return out
 
 

@@ -540,13 +540,19 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
-  const uint32_t rest = bid / (uint32_t)p.n_qtiles;
+  const uint32_t rest0 = bid / (uint32_t)p.n_qtiles;
+  const int32_t span = (int32_t)(rest0 % (uint32_t)p.n_spans);
+  const uint32_t rest = rest0 / (uint32_t)p.n_spans;
   const int32_t g = (int32_t)(rest % (uint32_t)p.ga.n_groups);
   const int64_t bh = (int64_t)(rest / (uint32_t)p.ga.n_groups);
   const GroupGeom geo = group_geom(p.ga, g);
-  const int32_t qbase = qt * p.q_tile;
-  if (qbase >= geo.len) return;   // uniform over the workgroup
-  const int32_t qend = min(geo.len, qbase + p.q_tile);
+  // queries [span_lo, span_hi) of the group; keys [0, klen)
+  const int32_t span_lo = p.q_first + span * p.q_span;
+  const int32_t span_hi = p.q_span > 0 ? min(geo.len, span_lo + p.q_span) : geo.len;
+  const int32_t klen = span_hi;
+  const int32_t qbase = span_lo + qt * p.q_tile;
+  if (qbase >= span_hi) return;   // uniform over the workgroup
+  const int32_t qend = min(span_hi, qbase + p.q_tile);
   const RowMap rm = row_map(geo);
 
   const unsigned char *qbytes = uniform_ptr(
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const int32_t qm = q0 + col;
   const bool wave_active = q0 < qend;   // wave-uniform
 
-  const int32_t n = (geo.len + kKeyTile - 1) / kKeyTile;
+  const int32_t n = (klen + kKeyTile - 1) / kKeyTile;
   // Prologue. The workgroup's 32*NW query rows come in like key tiles (whole
   // rows per DMA window, rather than 16 bytes of 64 rows per load) into the
   // buffers of value tile 1 and key tile 2, which stay free until step 0
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
       auto on_pv = [&](int i) __attribute__((always_inline)) {
         if (i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
-      stream_tile<D>(kc, yc, qb, t * kKeyTile, geo.len, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
+      stream_tile<D>(kc, yc, qb, t * kKeyTile, klen, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
                      on_qk, on_pv);
 #pragma unroll
       for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);

@@ -16,8 +16,15 @@ struct AttnLaunch {
   void *out;
   int64_t head_elems; // N * head_dim: distance between consecutive (batch, head) slices
   GroupAddr ga;
-  int32_t n_qtiles;   // query tiles per group (sized for the largest group)
+  int32_t n_qtiles;   // query tiles per group, or per query span (sized for the largest)
   int32_t q_tile;     // queries per query tile (streaming bf16 kernel)
+  // Query ranges of the streaming bf16 kernel (other kernels take 0, 0, 1):
+  // members below q_first are keys only; with q_span > 0 the queries from
+  // q_first on are cut into n_spans spans of q_span members, and span s
+  // attends to members [0, q_first + (s+1) q_span) only (chunk-causal).
+  int32_t q_first;
+  int32_t q_span;
+  int32_t n_spans;
   int32_t n_bh;       // batch * heads
   float scale;        // 1/sqrt(head_dim)
   float scale_log2;   // scale * log2(e): softmax evaluated with exp2

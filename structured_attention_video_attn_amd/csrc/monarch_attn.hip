@@ -110,15 +110,30 @@ bool two_level(const Problem &p, const GroupAddr &ga) {
   return outer || ga.max_len >= (1 << 24) || mstride >= (1 << 24);
 }
 
+// Query ranges (streaming bf16 kernel only): queries from member q_first on,
+// cut into spans of q_span members (0: one span) whose keys end with the span.
+struct QueryRange {
+  int32_t q_first = 0;
+  int32_t q_span = 0;
+  bool stream = false;   // take the streaming kernel even for short groups
+};
+
 int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void *k,
-                const void *vals, void *out, Plan *pl) {
+                const void *vals, void *out, Plan *pl, QueryRange qr = QueryRange{}) {
   AttnLaunch a{};
   a.q = q;
   a.k = k;
   a.vals = vals;
   a.out = out;
-  a.head_elems = p.N * p.D;
+  a.head_elems = p.slice_elems;
   a.ga = ga;
+  const bool ranged = qr.q_first > 0 || qr.q_span > 0 || qr.stream;
+  if (ranged && p.dtype != MA_BF16) return MA_ERR_UNSUPPORTED;
+  const int32_t queries = ga.max_len - qr.q_first;   // per group, from q_first on
+  const int32_t qlen = qr.q_span > 0 && qr.q_span < queries ? qr.q_span : queries;
+  a.q_first = qr.q_first;
+  a.q_span = qr.q_span > 0 && qr.q_span < queries ? qr.q_span : 0;
+  a.n_spans = a.q_span > 0 ? (queries + a.q_span - 1) / a.q_span : 1;
   a.n_bh = (int32_t)(p.batch * p.heads);
   a.scale = (float)(1.0 / sqrt((double)p.D));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
@@ -126,7 +141,7 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
   if (p.dtype == MA_F32) {
     q_per_block = kF32Threads;
     pl->kernel = Kernel::kF32;
-  } else if (ga.max_len <= kKeyTile) {
+  } else if (ga.max_len <= kKeyTile && !ranged) {
     q_per_block = kKeyTile;   // one group per work item
     pl->kernel = Kernel::kBlock;
   } else {
@@ -139,8 +154,8 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
     // allows (D/8 16-byte chunks per row).
     const int max_waves = p.D >= 32 ? 4 : 2;
     const int64_t cap = (int64_t)kQueriesPerWave * max_waves;
-    const int64_t per_group = (ga.max_len + cap - 1) / cap;
-    const int64_t share = (ga.max_len + per_group - 1) / per_group;
+    const int64_t per_group = (qlen + cap - 1) / cap;
+    const int64_t share = (qlen + per_group - 1) / per_group;
     const int64_t need = (share + kQueriesPerWave - 1) / kQueriesPerWave;
     int w = 2;
     while (w < need && w < max_waves) w *= 2;
@@ -149,9 +164,10 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
     pl->kernel = Kernel::kStream;
     pl->two_level = two_level(p, ga);
   }
-  a.n_qtiles = (ga.max_len + q_per_block - 1) / q_per_block;
+  a.n_qtiles = (qlen + q_per_block - 1) / q_per_block;
   a.q_tile = q_per_block;
-  const uint64_t blocks = (uint64_t)a.n_qtiles * (uint64_t)ga.n_groups * (uint64_t)a.n_bh;
+  const uint64_t blocks =
+      (uint64_t)a.n_qtiles * (uint64_t)a.n_spans * (uint64_t)ga.n_groups * (uint64_t)a.n_bh;
   if (blocks > (uint64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
   pl->blocks = (uint32_t)blocks;
   pl->n_items = (int32_t)blocks;
@@ -174,13 +190,28 @@ int copy_async(void *dst, const void *src, size_t bytes, hipStream_t s) {
   return hip_status(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
 }
 
+// Stage-L members per frame (b1 / T): a group holds one member per (frame, row)
+// at r_axes = 1, one per frame at 2, one per token at 0.
+int64_t members_per_frame(const Problem &p) { return p.T > 0 ? p.b1 / p.T : 0; }
+
+// chunk_t > 0: chunk-causal stage L (bf16, r_axes 0..2): a query in chunk c
+// attends to the members of its group in chunks 0..c.
 int monarch_common(const void *q, const void *k, const void *v, void *out, void *ws, size_t ws_bytes,
                    int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W, int32_t r_axes,
                    int32_t tile_t, int32_t tile_h, bool tiled, int32_t head_dim, int32_t dtype,
-                   hipStream_t stream) {
+                   hipStream_t stream, int32_t chunk_t = 0) {
   Problem p;
   int st = resolve_grid(batch, heads, T, H, W, r_axes, tile_t, tile_h, tiled, head_dim, dtype, &p);
-  if (st != MA_OK || p.empty) return st;
+  if (st != MA_OK) return st;
+  QueryRange lr;
+  if (chunk_t != 0) {
+    if (chunk_t < 0 || r_axes > 2 || tiled) return MA_ERR_INVALID_ARG;
+    if (dtype != MA_BF16) return MA_ERR_UNSUPPORTED;
+    const int64_t span = (int64_t)chunk_t * members_per_frame(p);
+    lr.q_span = span < p.b1 ? (int32_t)span : 0;
+    lr.stream = true;
+  }
+  if (p.empty) return MA_OK;
   st = check_tensor_ptrs(q, k, v, out, p.tensor_bytes);
   if (st != MA_OK) return st;
   const size_t need = workspace_needed(p);
@@ -200,7 +231,7 @@ int monarch_common(const void *q, const void *k, const void *v, void *out, void 
     if (st != MA_OK) return st;
   }
   if (run_l) {
-    st = plan_launch(p, stage_l_groups(p), q, k, y_in, out, &pl);
+    st = plan_launch(p, stage_l_groups(p), q, k, y_in, out, &pl, lr);
     if (st != MA_OK) return st;
   }
   if (!run_r && !run_l) return copy_async(out, v, p.tensor_bytes, stream);
@@ -353,6 +384,64 @@ int monarch_attn_tiled_fwd(const void *q, const void *k, const void *v, void *ou
                            int32_t dtype, struct ihipStream_t *stream) {
   return monarch_common(q, k, v, out, workspace, workspace_bytes, batch, heads, T, H, W, 1, tile_t,
                         tile_h, true, head_dim, dtype, stream);
+}
+
+int monarch_attn_causal_fwd(const void *q, const void *k, const void *v, void *out, void *workspace,
+                            size_t workspace_bytes, int32_t batch, int32_t heads, int32_t T, int32_t H,
+                            int32_t W, int32_t r_axes, int32_t chunk_t, int32_t head_dim, int32_t dtype,
+                            struct ihipStream_t *stream) {
+  if (chunk_t < 1) return MA_ERR_INVALID_ARG;
+  return monarch_common(q, k, v, out, workspace, workspace_bytes, batch, heads, T, H, W, r_axes, 0, 0,
+                        false, head_dim, dtype, stream, chunk_t);
+}
+
+int monarch_attn_chunk_fwd(const void *q, const void *k, const void *v, void *y, void *out, int32_t batch,
+                           int32_t heads, int32_t T, int32_t H, int32_t W, int32_t r_axes, int32_t t0,
+                           int32_t chunk_t, int32_t head_dim, int32_t dtype, struct ihipStream_t *stream) {
+  Problem p;
+  int st = resolve_grid(batch, heads, T, H, W, r_axes, 0, 0, false, head_dim, dtype, &p);
+  if (st != MA_OK) return st;
+  if (r_axes > 2 || chunk_t < 1 || t0 < 0 || (int64_t)t0 + chunk_t > T) return MA_ERR_INVALID_ARG;
+  if (dtype != MA_BF16) return MA_ERR_UNSUPPORTED;
+  if (p.empty) return MA_OK;
+  st = check_tensor_ptrs(q, k, v, out, p.tensor_bytes);
+  if (st != MA_OK) return st;
+  const bool use_y = !p.r_trivial;   // at r_axes = 0, Y is V and y is not used
+  if (use_y) {
+    if (y == nullptr) return MA_ERR_INVALID_ARG;
+    if (!aligned16(y)) return MA_ERR_ALIGNMENT;
+    if (overlaps(y, q, p.tensor_bytes) || overlaps(y, k, p.tensor_bytes) || overlaps(y, v, p.tensor_bytes) ||
+        overlaps(y, out, p.tensor_bytes))
+      return MA_ERR_INVALID_ARG;
+  }
+  // stage R over the chunk's frames: the same buffers seen from frame t0, with
+  // the full buffers' distance between (batch, head) slices
+  Problem pc;
+  st = resolve_grid(batch, heads, chunk_t, H, W, r_axes, 0, 0, false, head_dim, dtype, &pc);
+  if (st != MA_OK) return st;
+  pc.slice_elems = p.slice_elems;
+  // stage L over the frames [0, t0 + chunk_t), queries from the chunk's first member on
+  Problem pl;
+  st = resolve_grid(batch, heads, t0 + chunk_t, H, W, r_axes, 0, 0, false, head_dim, dtype, &pl);
+  if (st != MA_OK) return st;
+  pl.slice_elems = p.slice_elems;
+  QueryRange lr;
+  lr.q_first = (int32_t)((int64_t)t0 * members_per_frame(pl));
+  lr.stream = true;
+  const size_t off = (size_t)t0 * (size_t)(H * W) * (size_t)head_dim * p.elem_bytes;
+  auto at = [off](const void *x) { return static_cast<const unsigned char *>(x) + off; };
+  Plan pr{}, pll{};
+  if (use_y) {
+    st = plan_launch(pc, stage_r_groups(pc), at(q), at(k), at(v), static_cast<unsigned char *>(y) + off, &pr);
+    if (st != MA_OK) return st;
+  }
+  st = plan_launch(pl, stage_l_groups(pl), q, k, use_y ? (const void *)y : v, out, &pll, lr);
+  if (st != MA_OK) return st;
+  if (use_y) {
+    st = run_plan(pc, pr, stream);
+    if (st != MA_OK) return st;
+  }
+  return run_plan(pl, pll, stream);
 }
 
 int dense_attn_fwd(const void *q, const void *k, const void *v, void *out, int32_t batch,

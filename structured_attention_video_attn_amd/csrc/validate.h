@@ -19,6 +19,8 @@ struct Problem {
   int32_t dtype;
   size_t elem_bytes;
   size_t tensor_bytes;      // bytes of one [batch, heads, N, D] tensor
+  int64_t slice_elems;      // elements between (batch, head) slices: N * D, or the full
+                            // buffer's when the grid is a frame range of a longer one
   bool empty;               // some extent is zero: nothing to do
   bool r_trivial;           // b2 == 1: Y = V
   bool l_trivial;           // every stage-L group has one member: O = Y
@@ -70,6 +72,7 @@ inline int resolve_grid(int32_t batch, int32_t heads, int32_t T, int32_t H, int3
   if (p->N * p->D > (int64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
   if ((int64_t)batch * heads > (int64_t)INT32_MAX / 2) return MA_ERR_UNSUPPORTED;
   p->tensor_bytes = (size_t)batch * (size_t)heads * (size_t)p->N * (size_t)head_dim * p->elem_bytes;
+  p->slice_elems = p->N * p->D;
   switch (r_axes) {
     case 0: p->b2 = 1; break;
     case 1: p->b2 = W; break;

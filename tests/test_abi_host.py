@@ -220,3 +220,31 @@ def test_binding_fails_loudly_without_library(tmp_path):
     from structured_attention_video_attn_amd import _binding
     with pytest.raises(RuntimeError, match="not built"):
         _binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_causal_and_chunk_argument_errors(lib):
+    # every call fails an argument check or is empty: nothing is launched
+    q, k, v, o, w = _ptrs()
+    nb = 12 * 32760 * 128 * 2
+    c = lib.monarch_attn_causal_fwd
+    assert c(q, k, v, o, w, nb, 1, 12, 21, 30, 52, 1, 0, 128, BF16, None) == INVALID     # chunk_t < 1
+    assert c(q, k, v, o, w, nb, 1, 12, 21, 30, 52, 3, 3, 128, BF16, None) == INVALID     # r_axes 3
+    assert c(q, k, v, o, w, nb, 1, 12, 21, 30, 52, 1, 3, 128, F32, None) == UNSUPPORTED
+    assert c(q, k, v, q, w, nb, 1, 12, 21, 30, 52, 1, 3, 128, BF16, None) == INVALID     # out aliases q
+    assert c(q, k, v, o, None, 0, 1, 12, 21, 30, 52, 1, 3, 128, BF16, None) == WORKSPACE
+    assert c(None, None, None, None, None, 0, 0, 12, 21, 30, 52, 1, 3, 128, BF16, None) == OK
+    s = lib.monarch_attn_chunk_fwd
+    y = w
+    good = (1, 12, 21, 30, 52)
+    assert s(q, k, v, y, o, *good, 3, 18, 3, 128, BF16, None) == INVALID       # r_axes 3
+    assert s(q, k, v, y, o, *good, 1, -1, 3, 128, BF16, None) == INVALID      # t0 < 0
+    assert s(q, k, v, y, o, *good, 1, 19, 3, 128, BF16, None) == INVALID      # past the last frame
+    assert s(q, k, v, y, o, *good, 1, 18, 0, 128, BF16, None) == INVALID      # chunk_t < 1
+    assert s(q, k, v, y, o, *good, 1, 18, 3, 128, F32, None) == UNSUPPORTED
+    assert s(q, k, v, None, o, *good, 1, 18, 3, 128, BF16, None) == INVALID   # y needed at r_axes 1
+    assert s(q, k, v, o, o, *good, 1, 18, 3, 128, BF16, None) == INVALID     # y aliases out
+    assert s(q, k, v, v, o, *good, 1, 18, 3, 128, BF16, None) == INVALID     # y aliases v
+    assert s(q, k, v, y + 8, o, *good, 1, 18, 3, 128, BF16, None) == ALIGN
+    assert s(q, k, v, y, q, *good, 1, 18, 3, 128, BF16, None) == INVALID     # out aliases q
+    assert s(q, k, v, y, o, 1, 12, 21, 30, 52, 1, 18, 3, 48, BF16, None) == UNSUPPORTED
+    assert s(None, None, None, None, None, 0, 12, 21, 30, 52, 1, 18, 3, 128, BF16, None) == OK
