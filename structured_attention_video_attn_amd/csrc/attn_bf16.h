@@ -70,6 +70,7 @@ typedef uint16_t u16;
 constexpr int kKeyTile = 64;       // keys per LDS tile
 constexpr int kQueriesPerWave = 32;
 constexpr int kBlockWaves = 2;     // waves per block_attn_bf16 workgroup
+constexpr int kBlockResident = 4;  // resident block_attn_bf16 workgroups per CU (LDS 32 KB, <= 256 VGPRs)
 constexpr float kLazyRescale = 8.f;
 
 template <int D>
@@ -94,27 +95,6 @@ __device__ __forceinline__ int swizzle_chunk(int r, int c) {
 __device__ __forceinline__ float swap_halves(float x) {   // value of lane l ^ 32
   auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
-}
-
-// DMA of group rows [k0, k0 + 64) of one tensor into an LDS tile (waves of the
-// workgroup split the 1 KB windows). kSkipPast: windows wholly past the group
-// are skipped (their rows must already hold finite data); otherwise rows past
-// the group repeat its last member. Either way those rows are masked later.
-template <int D, bool kSkipPast>
-__device__ __forceinline__ void dma_tile(const unsigned char *src, unsigned char *dst,
-                                         const GroupGeom &geo, int32_t k0, int wave, int lane, int nw) {
-  using G = TileGeo<D>;
-  for (int ii = wave; ii < G::NINST; ii += nw) {
-    if (kSkipPast && k0 + ii * G::ROWS_PER_INST >= geo.len) break;   // wave-uniform
-    const int slot = ii * 64 + lane;
-    const int r = slot / G::CPR, pos = slot % G::CPR;
-    const int c = swizzle_chunk<G::CPR>(r, pos);
-    const int32_t km = min(k0 + r, geo.len - 1);
-    // offsets inside one (batch, head) slice fit in 32 bits (N * D < 2^31 elements)
-    const uint32_t off = ((uint32_t)member_token(geo, km) * D + c * 8) * 2u;
-    __builtin_amdgcn_global_load_lds((MA_GLOBAL void *)(src + off), (MA_LDS void *)(dst + ii * 1024), 16,
-                                     0, 0);
-  }
 }
 
 // This lane's query as the B operand of S^T = K Q^T: head_dim slots
@@ -721,21 +701,20 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent kernel for groups of at most 64 tokens. Workgroup w handles items
-// w, w + G, w + 2G, ... (item = group + n_groups * (batch*head)); the keys and
-// values of item i+G go into the other LDS buffer pair, and its queries into
-// registers, while item i is computed. A wave waits for that prefetch only
-// after its compute, when it has had a whole item to land; the barrier opening
-// the next item then publishes it to both waves. Outputs leave through the
-// item's key buffer as whole rows rather than 8 bytes of 64 rows per store.
+// Persistent kernel for groups of at most 64 tokens (stage R at W <= 64, short
+// stage-L groups). Workgroup w handles items w, w + G, w + 2G, ... (item =
+// group + n_groups * (batch*head)), one at a time: K and V tiles by DMA, the
+// queries into registers, the softmax attention of the group, the output
+// staged row-major in the key buffer and stored as whole rows. There is no
+// prefetch: four resident workgroups per CU (32 KB of LDS and two waves each)
+// keep more loads in flight than two double-buffered ones did, and the stage
+// runs at about the rate of a device-to-device copy.
 template <int D>
 __global__ __launch_bounds__(kBlockWaves * 64, 2) void block_attn_bf16(AttnLaunch p, int32_t n_items) {
   using G = TileGeo<D>;
   constexpr int NW = kBlockWaves;
-  __shared__ __align__(1024) unsigned char kt0[G::TILEB];
-  __shared__ __align__(1024) unsigned char kt1[G::TILEB];
-  __shared__ __align__(1024) unsigned char yt0[G::TILEB];
-  __shared__ __align__(1024) unsigned char yt1[G::TILEB];
+  __shared__ __align__(1024) unsigned char kt[G::TILEB];
+  __shared__ __align__(1024) unsigned char yt[G::TILEB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -745,61 +724,43 @@ __global__ __launch_bounds__(kBlockWaves * 64, 2) void block_attn_bf16(AttnLaunc
 
   // Rows past a group are never loaded; start from finite (zero) tiles.
   for (int i = threadIdx.x; i < G::TILEB / 16; i += NW * 64) {
-    reinterpret_cast<uint4 *>(kt0)[i] = make_uint4(0, 0, 0, 0);
-    reinterpret_cast<uint4 *>(kt1)[i] = make_uint4(0, 0, 0, 0);
-    reinterpret_cast<uint4 *>(yt0)[i] = make_uint4(0, 0, 0, 0);
-    reinterpret_cast<uint4 *>(yt1)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4 *>(kt)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4 *>(yt)[i] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
-  int32_t item = blockIdx.x;
-  if (item >= n_items) return;   // uniform
-  const int32_t stride = gridDim.x;
-
-  struct Item {
-    GroupGeom geo;
-    int64_t bh;
-  };
-  auto decode = [&](int32_t it) {
-    Item r;
-    r.geo = group_geom(p.ga, it % p.ga.n_groups);
-    r.bh = it / p.ga.n_groups;
-    return r;
-  };
-  auto issue = [&](const Item &it, unsigned char *kd, unsigned char *yd, bf16x8_t *qdst) {
+  for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const GroupGeom geo = group_geom(p.ga, item % p.ga.n_groups);
+    const int64_t bh = item / p.ga.n_groups;
     const unsigned char *kb =
-        reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + it.bh * p.head_elems);
+        reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.k) + bh * p.head_elems);
     const unsigned char *vb =
-        reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + it.bh * p.head_elems);
-    dma_tile<D, true>(kb, kd, it.geo, 0, wave, lane, NW);
-    dma_tile<D, true>(vb, yd, it.geo, 0, wave, lane, NW);
-    load_query<D>(static_cast<const u16 *>(p.q) + it.bh * p.head_elems, it.geo,
-                  wave * kQueriesPerWave + col, half, qdst);
-  };
-
-  Item cur = decode(item);
-  bf16x8_t qb[G::DK], qn[G::DK];
-  issue(cur, kt0, yt0, qb);
-  wait_dma();
-
-  auto phase = [&](const unsigned char *kc, const unsigned char *yc, unsigned char *kn, unsigned char *yn) {
-    __syncthreads();   // the item's tiles are visible to both waves; kn/yn are no longer read
-    const int32_t nxt = item + stride;
-    Item next = cur;
-    if (nxt < n_items) {
-      next = decode(nxt);
-      issue(next, kn, yn, qn);
+        reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + bh * p.head_elems);
+    {
+      // windows wholly past the group are skipped (their rows keep finite
+      // data from earlier items or the zero fill; they are masked)
+      const unsigned char *ku = uniform_ptr(kb), *vu = uniform_ptr(vb);
+      for (int ii = wave; ii < G::NINST; ii += NW) {
+        if (ii * G::ROWS_PER_INST >= geo.len) break;   // wave-uniform
+        const int slot = ii * 64 + lane;
+        const int r = slot / G::CPR, pos = slot % G::CPR;
+        const int c = swizzle_chunk<G::CPR>(r, pos);
+        const uint32_t off = ((uint32_t)member_token(geo, min(r, geo.len - 1)) * D + c * 8) * 2u;
+        dma16(ku, off, kt + ii * 1024);
+        dma16(vu, off, yt + ii * 1024);
+      }
     }
+    bf16x8_t qb[G::DK];
+    load_query<D>(static_cast<const u16 *>(p.q) + bh * p.head_elems, geo, wave * kQueriesPerWave + col, half, qb);
+    wait_dma();
+    __syncthreads();   // the tiles are visible to both waves
     f32x16_t oacc[G::DB];
 #pragma unroll
     for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;
-    attend_tile<D>(kc, yc, qb, 0, cur.geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key, tr_col);
-    wait_dma();        // the prefetch of `next` (and older stores) completed
-    __syncthreads();   // both waves are done with kc: it stages the output
-    // normalised 32 x D tile of this wave, row-major with XOR-swizzled
-    // chunks, then stored as whole rows (D/8 lanes per row)
-    unsigned char *ot = const_cast<unsigned char *>(kc) + wave * 32 * G::ROWB;
+    attend_tile<D>(kt, yt, qb, 0, geo.len, p.scale_log2, m_run, l_run, oacc, col, half, tr_key, tr_col);
+    __syncthreads();   // both waves are done with kt: it stages the output
+    unsigned char *ot = kt + wave * 32 * G::ROWB;
     const float inv = 1.f / (l_run + swap_halves(l_run));
 #pragma unroll
     for (int b = 0; b < G::DB; ++b)
@@ -814,26 +775,16 @@ __global__ __launch_bounds__(kBlockWaves * 64, 2) void block_attn_bf16(AttnLaunc
           *reinterpret_cast<bf16x4_t *>(ot + col * G::ROWB + 16 * chunk + 8 * half) = v;
         }
       }
-    u16 *oh = static_cast<u16 *>(p.out) + cur.bh * p.head_elems;
-    constexpr int RPI = 64 / G::CPR;   // rows per store instruction
+    u16 *oh = static_cast<u16 *>(p.out) + bh * p.head_elems;
+    constexpr int RPI = 64 / G::CPR;
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int r = r0 + lane / G::CPR, c = lane % G::CPR;
       const uint4 v = *reinterpret_cast<const uint4 *>(ot + r * G::ROWB + 16 * (c ^ (r & (G::CPR - 1))));
       const int32_t m = wave * kQueriesPerWave + r;
-      if (m < cur.geo.len) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(cur.geo, m) * D + 8 * c) = v;
+      if (m < geo.len) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(geo, m) * D + 8 * c) = v;
     }
-#pragma unroll
-    for (int j = 0; j < G::DK; ++j) qb[j] = qn[j];
-    cur = next;
-    item = nxt;
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  while (true) {
-    phase(kt0, yt0, kt1, yt1);
-    if (item >= n_items) break;
-    phase(kt1, yt1, kt0, yt0);
-    if (item >= n_items) break;
+    __syncthreads();   // the staged rows are read before the next item's keys land in kt
   }
 }
 

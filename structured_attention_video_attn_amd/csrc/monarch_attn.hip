@@ -44,7 +44,7 @@ struct Plan {
 };
 
 // Compute units of the current device, cached per device (the persistent
-// kernel launches two resident workgroups per CU).
+// kernel launches kBlockResident workgroups per CU).
 int device_cus(int *cus) {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -76,7 +76,7 @@ int launch_d(const Plan &pl, hipStream_t s) {
       int cus = 0;
       const int st = device_cus(&cus);
       if (st != MA_OK) return st;
-      const uint32_t resident = 2u * (uint32_t)cus;
+      const uint32_t resident = kBlockResident * (uint32_t)cus;
       const uint32_t blocks = pl.blocks < resident ? pl.blocks : resident;
       hipLaunchKernelGGL(block_attn_bf16<D>, dim3(blocks), dim3(kBlockWaves * 64), 0, s, pl.a, pl.n_items);
       break;
