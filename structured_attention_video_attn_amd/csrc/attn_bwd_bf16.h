@@ -348,12 +348,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16(BwdLaunch p) {
 // dK/dV pass. Double buffers: query tiles in LDS tiles 0..1, dO tiles in
 // 2..3, and the (lse, D) window of each dO tile (128 members x 8 bytes, of
 // which the tile uses 64) in two 1 KB slots; step t issues dO, stats and Q of
-// tile t+1. At head_dim 128 its live registers (dK^T and dV^T accumulators,
-// this wave's key and value rows, S and dP of a tile) exceed the 256 that two
-// waves per SIMD allow, and spilling costs more than the lost occupancy, so
-// it runs one wave per SIMD there; smaller head dims fit two.
-template <int D, int NW, bool kTwoLevel>
-__global__ __launch_bounds__(NW * 64, D >= 128 ? 1 : 2) void bwd_dkdv_bf16(BwdLaunch p) {
+// tile t+1. kPart selects the outputs: 0 both, 1 dK only, 2 dV only. With
+// both, the live registers at head_dim 128 (dK^T and dV^T accumulators, this
+// wave's key and value rows, S and dP of a tile) exceed the 256 that two
+// waves per SIMD allow; each single-output part fits them, at the price of a
+// second S (the dV part needs neither V rows nor dP).
+template <int D, int NW, bool kTwoLevel, int kPart>
+__global__ __launch_bounds__(NW * 64, (D >= 128 && kPart == 0) ? 1 : 2) void bwd_dkdv_bf16(BwdLaunch p) {
+  constexpr bool kDK = kPart != 2, kDV = kPart != 1;
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
   constexpr int DK = G::DK, DB = G::DB;
@@ -395,15 +397,21 @@ __global__ __launch_bounds__(NW * 64, D >= 128 ? 1 : 2) void bwd_dkdv_bf16(BwdLa
   stats_window(0, 0);
   bf16x8_t kb[DK], vb[DK];
   load_row_frags<D>(static_cast<const u16 *>(p.k) + slice, geo, km, half, kb);
-  load_row_frags<D>(static_cast<const u16 *>(p.v) + slice, geo, km, half, vb);
+  if constexpr (kDK) load_row_frags<D>(static_cast<const u16 *>(p.v) + slice, geo, km, half, vb);
   wait_vmcnt<0>();
 #pragma unroll
-  for (int j = 0; j < DK; ++j) asm volatile("" ::"v"(kb[j]), "v"(vb[j]));
+  for (int j = 0; j < DK; ++j) {
+    asm volatile("" ::"v"(kb[j]));
+    if constexpr (kDK) asm volatile("" ::"v"(vb[j]));
+  }
   __syncthreads();
 
   f32x16_t dka[DB], dva[DB];
 #pragma unroll
-  for (int b = 0; b < DB; ++b) dka[b] = dva[b] = f32x16_t{};
+  for (int b = 0; b < DB; ++b) {
+    if constexpr (kDK) dka[b] = f32x16_t{};
+    if constexpr (kDV) dva[b] = f32x16_t{};
+  }
   for (int32_t t = 0; t < n; ++t) {
     if (t > 0) wait_vmcnt<0>();   // tile t: the only DMAs in flight
     __syncthreads();              // ... landed for every wave, and tile t-1's buffers are free
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, D >= 128 ? 1 : 2) void bwd_dkdv_bf16(BwdLa
     if (wave_active) {
       f32x16_t s0, s1, t0, t1;
       tile_times<D>(qc, kb, lo, s0, s1);   // S: rows = queries of the tile, columns = this wave's keys
-      tile_times<D>(dc, vb, lo, t0, t1);   // dP
+      if constexpr (kDK) tile_times<D>(dc, vb, lo, t0, t1);   // dP
       bf16x8_t p0[2], p1[2], g0[2], g1[2];
       const int32_t q0t = t * kKeyTile;
 #pragma unroll
@@ -434,40 +442,43 @@ __global__ __launch_bounds__(NW * 64, D >= 128 ? 1 : 2) void bwd_dkdv_bf16(BwdLa
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
             const float sv = blk ? s1[r] : s0[r];
-            const float tv = blk ? t1[r] : t0[r];
             // (lse, D) of members past the group are never written: select them away
             // before any arithmetic so that whatever bytes they hold cannot propagate
             const bool valid = q0t + row + e < geo.len;
-            const float lv = valid ? lse[e] : 0.f, dv_ = valid ? dd[e] : 0.f;
+            const float lv = valid ? lse[e] : 0.f;
             const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sv, p.scale_log2, -lv)) : 0.f;
             pv[e] = pr;
-            gv[e] = pr * (tv - dv_);
+            if constexpr (kDK) {
+              const float tv = blk ? t1[r] : t0[r];
+              gv[e] = pr * (tv - (valid ? dd[e] : 0.f));
+            }
           }
-          if (blk) {
-            pack_pair(pv[0], pv[1], 4 * r4, p1);
-            pack_pair(pv[2], pv[3], 4 * r4 + 2, p1);
-            pack_pair(gv[0], gv[1], 4 * r4, g1);
-            pack_pair(gv[2], gv[3], 4 * r4 + 2, g1);
-          } else {
-            pack_pair(pv[0], pv[1], 4 * r4, p0);
-            pack_pair(pv[2], pv[3], 4 * r4 + 2, p0);
-            pack_pair(gv[0], gv[1], 4 * r4, g0);
-            pack_pair(gv[2], gv[3], 4 * r4 + 2, g0);
+          bf16x8_t(&pp)[2] = blk ? p1 : p0;
+          bf16x8_t(&gg)[2] = blk ? g1 : g0;
+          if constexpr (kDV) {
+            pack_pair(pv[0], pv[1], 4 * r4, pp);
+            pack_pair(pv[2], pv[3], 4 * r4 + 2, pp);
+          }
+          if constexpr (kDK) {
+            pack_pair(gv[0], gv[1], 4 * r4, gg);
+            pack_pair(gv[2], gv[3], 4 * r4 + 2, gg);
           }
         }
       }
-      tile_t_times<D>(dc, p0, p1, lo, tr_col, dva);   // dV^T += dO^T P
-      tile_t_times<D>(qc, g0, g1, lo, tr_col, dka);   // dK^T += Q^T dS
+      if constexpr (kDV) tile_t_times<D>(dc, p0, p1, lo, tr_col, dva);   // dV^T += dO^T P
+      if constexpr (kDK) tile_t_times<D>(qc, g0, g1, lo, tr_col, dka);   // dK^T += Q^T dS
     }
   }
   wait_vmcnt<0>();
   __syncthreads();
   // dK = s * dKacc, dV = dVacc, each through LDS (waves use separate 32-row fp32 areas)
   unsigned char *ot = lds + wave * 32 * (4 * D);
-  store_rows_lds<D>(ot, dka, p.scale, col, half, lane, static_cast<u16 *>(p.dk) + slice, geo, k0w, kend,
-                    p.accumulate != 0);
-  __syncthreads();
-  store_rows_lds<D>(ot, dva, 1.f, col, half, lane, static_cast<u16 *>(p.dv) + slice, geo, k0w, kend, false);
+  if constexpr (kDK)
+    store_rows_lds<D>(ot, dka, p.scale, col, half, lane, static_cast<u16 *>(p.dk) + slice, geo, k0w, kend,
+                      p.accumulate != 0);
+  if constexpr (kDK && kDV) __syncthreads();
+  if constexpr (kDV)
+    store_rows_lds<D>(ot, dva, 1.f, col, half, lane, static_cast<u16 *>(p.dv) + slice, geo, k0w, kend, false);
 }
 
 // ---------------------------------------------------------------------------

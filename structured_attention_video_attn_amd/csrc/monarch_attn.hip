@@ -287,11 +287,20 @@ int launch_bwd_d(bool dq_pass, bool two_level, const BwdLaunch &a, uint32_t bloc
       hipLaunchKernelGGL((bwd_dq_bf16<D, NW, true>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((bwd_dq_bf16<D, NW, false>), grid, block, 0, s, a);
+  } else if constexpr (D >= 128) {
+    // dV, then dK: each pass fits two waves per SIMD, where both together do not
+    if (two_level) {
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, true, 2>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, true, 1>), grid, block, 0, s, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, false, 2>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, false, 1>), grid, block, 0, s, a);
+    }
   } else {
     if (two_level)
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, true, 0>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, NW, false, 0>), grid, block, 0, s, a);
   }
   return hip_status(hipGetLastError());
 }
