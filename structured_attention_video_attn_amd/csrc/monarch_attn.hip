@@ -105,7 +105,10 @@ int launch_d(const Plan &pl, hipStream_t s) {
 // several outer rows (tiled boxes), or when member offsets do not fit the
 // 24-bit multiply of the one-level form.
 bool two_level(const Problem &p, const GroupAddr &ga) {
-  const bool outer = ga.len_o > 1 && ga.tile_o > 1;
+  // A box whose inner extent is whole (tile_i >= len_i) and whose outer stride
+  // continues the inner one is a single run: member m at base + m * stride_in.
+  const bool whole_rows = ga.tile_i >= ga.len_i && (int64_t)ga.stride_out == (int64_t)ga.len_i * ga.stride_in;
+  const bool outer = ga.len_o > 1 && ga.tile_o > 1 && !whole_rows;
   const int64_t mstride = (int64_t)ga.stride_in * 2 * p.D;
   return outer || ga.max_len >= (1 << 24) || mstride >= (1 << 24);
 }
