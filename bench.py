@@ -50,6 +50,8 @@ def parse_args():
                     help="run only this kernel (or a plain device copy of one input tensor, the "
                          "calibration for byte counters; or the whole backward) --steps times on "
                          "the 21x30x52 workload; for rocprofv3")
+    ap.add_argument("--profile-warmup", type=int, default=0,
+                    help="with --profile-only: launches before the --steps profiled ones (clock ramp)")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output (kernel runs and "
@@ -164,9 +166,10 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, ker
     print(json.dumps(out))
 
 
-def profile_only(which, steps, n_sets=3):
+def profile_only(which, steps, warmup=0, n_sets=3):
     """Run one kernel `steps` times over rotating buffer sets (about 1.5 GB in all,
-    more than the 256 MB MALL), so that every launch reads its inputs from HBM."""
+    more than the 256 MB MALL), so that every launch reads its inputs from HBM; the
+    first `warmup` of them only bring the clocks up."""
     import torch
     import structured_attention_video_attn_amd as ma
     from workloads import WORKLOADS, make_qkv
@@ -190,7 +193,7 @@ def profile_only(which, steps, n_sets=3):
         for q, k, v, y, o in sets:
             ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
     torch.cuda.synchronize()
-    for i in range(steps):
+    for i in range(warmup + steps):
         q, k, v, y, o = sets[i % n_sets]
         if which == "backward":
             ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W)
@@ -201,7 +204,7 @@ def profile_only(which, steps, n_sets=3):
         else:
             o.copy_(q)
     torch.cuda.synchronize()
-    print("profiled %s x%d" % (which, steps), flush=True)
+    print("profiled %s x%d (after %d more)" % (which, steps, warmup), flush=True)
 
 
 def main():
@@ -210,7 +213,7 @@ def main():
         summarize_counters(*args.summarize_counters, kernel=args.kernel)
         return
     if args.profile_only:
-        profile_only(args.profile_only, args.steps)
+        profile_only(args.profile_only, args.steps, args.profile_warmup)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the method is measured on a single MI355X and "
