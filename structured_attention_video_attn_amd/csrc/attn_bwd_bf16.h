@@ -22,6 +22,8 @@
 // group does both passes' work from one LDS copy of the group.
 // Rows outside the group are clamped duplicates (finite) and get zero weight.
 #pragma once
+#include <type_traits>
+
 #include "attn_bf16.h"
 
 namespace ma {
@@ -277,8 +279,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16(BwdLaunch p) {
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
-  int ks = 0, ys = 0;
-  for (int32_t t = 0; t < n; ++t) {
+  // Tile t: keys in buffer t % 3, values in 3 + t % 2; unrolled by six so that
+  // every buffer is a constant offset of the fragment reads.
+  auto step = [&](int32_t t, auto ks_c, auto ys_c) __attribute__((always_inline)) {
+    constexpr int ks = decltype(ks_c)::value, ys = decltype(ys_c)::value;
     if (t > 0) wait_vmcnt<WPT>();   // leave the key windows of tile t+1 in flight
     __syncthreads();
     const unsigned char *kc = lds + ks * G::TILEB;
@@ -328,8 +332,22 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_bf16(BwdLaunch p) {
       }
       tile_t_times<D>(kc, w0, w1, lo, tr_col, acc);   // dQ^T += K^T w^T
     }
-    ks = ks == 2 ? 0 : ks + 1;
-    ys ^= 1;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int32_t t = 0; t < n; t += 6) {
+    step(t, I0{}, I0{});
+    if (t + 1 >= n) break;
+    step(t + 1, I1{}, I1{});
+    if (t + 2 >= n) break;
+    step(t + 2, I2{}, I0{});
+    if (t + 3 >= n) break;
+    step(t + 3, I0{}, I1{});
+    if (t + 4 >= n) break;
+    step(t + 4, I1{}, I0{});
+    if (t + 5 >= n) break;
+    step(t + 5, I2{}, I1{});
   }
   wait_vmcnt<0>();   // DMAs into buffers past the last tile
   __syncthreads();
@@ -412,10 +430,15 @@ __global__ __launch_bounds__(NW * 64, (D >= 128 && kPart == 0) ? 1 : 2) void bwd
     if constexpr (kDK) dka[b] = f32x16_t{};
     if constexpr (kDV) dva[b] = f32x16_t{};
   }
-  for (int32_t t = 0; t < n; ++t) {
+  // Tile t in buffers t % 2. Only the group's last query tile can hold rows
+  // past the group: the tiles before it take a form without the per-row
+  // validity selects, unrolled by two so that every buffer is a constant
+  // offset of the fragment reads.
+  auto step = [&](int32_t t, auto cur_c, auto ragged_c) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool kRagged = decltype(ragged_c)::value;
     if (t > 0) wait_vmcnt<0>();   // tile t: the only DMAs in flight
     __syncthreads();              // ... landed for every wave, and tile t-1's buffers are free
-    const int cur = t & 1;
     const unsigned char *qc = lds + cur * G::TILEB;
     const unsigned char *dc = lds + (2 + cur) * G::TILEB;
     const unsigned char *sc = st_lds + cur * 1024;
@@ -444,7 +467,7 @@ __global__ __launch_bounds__(NW * 64, (D >= 128 && kPart == 0) ? 1 : 2) void bwd
             const float sv = blk ? s1[r] : s0[r];
             // (lse, D) of members past the group are never written: select them away
             // before any arithmetic so that whatever bytes they hold cannot propagate
-            const bool valid = q0t + row + e < geo.len;
+            const bool valid = !kRagged || q0t + row + e < geo.len;
             const float lv = valid ? lse[e] : 0.f;
             const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sv, p.scale_log2, -lv)) : 0.f;
             pv[e] = pr;
@@ -468,6 +491,20 @@ __global__ __launch_bounds__(NW * 64, (D >= 128 && kPart == 0) ? 1 : 2) void bwd
       if constexpr (kDV) tile_t_times<D>(dc, p0, p1, lo, tr_col, dva);   // dV^T += dO^T P
       if constexpr (kDK) tile_t_times<D>(qc, g0, g1, lo, tr_col, dka);   // dK^T += Q^T dS
     }
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  const int32_t n_full = geo.len / kKeyTile;   // query tiles with every row inside the group
+  int32_t t = 0;
+  for (; t + 2 <= n_full; t += 2) {
+    step(t, C0{}, std::false_type{});
+    step(t + 1, C1{}, std::false_type{});
+  }
+  for (; t < n; ++t) {   // at most one full tile and the ragged one
+    if (t & 1)
+      step(t, C1{}, std::true_type{});
+    else
+      step(t, C0{}, std::true_type{});
   }
   wait_vmcnt<0>();
   __syncthreads();
