@@ -85,11 +85,22 @@ struct TileGeo {
 };
 
 // Position of 16-byte chunk c of tile row r (CPR chunks per row, a power of 2).
+// The LDS serves 256 bytes (64 banks) per cycle. At head_dim 128 a tile row is
+// those 256 bytes, and row 4q + p (p, q < 4, row taken mod 16) gets the mask
+// 4p + q: any 16 consecutive rows get 16 different masks (a 16-byte read of
+// one chunk column serves 16 lanes per cycle, one row each), and the four
+// rows of an aligned quad get masks in four different quarters of the row (an
+// 8-byte transposed read serves 32 lanes per cycle over four rows and one
+// quarter of the chunks each), so neither read meets a bank twice.
 template <int CPR>
 __device__ __forceinline__ int swizzle_chunk(int r, int c) {
-  constexpr int kBits = CPR >= 2 ? __builtin_ctz(CPR) : 0;
-  const int s = ((r << 1) | ((r >> (kBits > 0 ? kBits - 1 : 0)) & 1)) & (CPR - 1);
-  return c ^ s;
+  if constexpr (CPR == 16) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    constexpr int kBits = CPR >= 2 ? __builtin_ctz(CPR) : 0;
+    const int s = ((r << 1) | ((r >> (kBits > 0 ? kBits - 1 : 0)) & 1)) & (CPR - 1);
+    return c ^ s;
+  }
 }
 
 __device__ __forceinline__ float swap_halves(float x) {   // value of lane l ^ 32
