@@ -172,11 +172,12 @@ __device__ __forceinline__ void load_row_frags(const u16 *base, const GroupGeom 
 // Writes this wave's 32 x D result through LDS as whole rows: acc holds it
 // transposed (acc[b] element r of lane (col, half) is head_dim 32b + 8(r/4) +
 // 4 half + r%4 of row col), scaled per column by `colscale`. Rows m0 + r with
-// m0 + r < mend go to base + token * D; with `add`, onto the values there.
+// m0 + r < mend go to base + token * D; with `add`, onto the values there, or
+// onto `old_rows` (those values, loaded earlier by load_old_rows).
 template <int D>
 __device__ __forceinline__ void store_rows_lds(unsigned char *ot, const f32x16_t *acc, float colscale, int col,
                                                int half, int lane, u16 *base, const GroupGeom &geo, int32_t m0,
-                                               int32_t mend, bool add) {
+                                               int32_t mend, bool add, const uint4 *old_rows = nullptr) {
   using G = TileGeo<D>;
 #pragma unroll
   for (int b = 0; b < G::DB; ++b)
@@ -204,7 +205,8 @@ __device__ __forceinline__ void store_rows_lds(unsigned char *ot, const f32x16_t
       u16 *dst = base + (uint32_t)member_token(geo, m) * D + 8 * c;
       float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       if (add) {
-        const bf16x8_t old = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(dst));
+        const bf16x8_t old =
+            __builtin_bit_cast(bf16x8_t, old_rows ? old_rows[r0 / RPI] : *reinterpret_cast<const uint4 *>(dst));
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] += (float)old[e];
       }
@@ -217,6 +219,23 @@ __device__ __forceinline__ void store_rows_lds(unsigned char *ot, const f32x16_t
       }
       *reinterpret_cast<uint4 *>(dst) = __builtin_bit_cast(uint4, outv);
     }
+  }
+}
+
+// The values store_rows_lds(..., add) would read back, in its order: rows
+// m0 + r (r = r0 + lane / (D/8), r0 = 0, 64/(D/8), ...; m0 + r < mend), 16 bytes
+// each at chunk lane % (D/8); zero for rows past mend.
+template <int D>
+__device__ __forceinline__ void load_old_rows(const u16 *base, const GroupGeom &geo, int32_t m0, int32_t mend,
+                                              int lane, uint4 *old_rows) {
+  using G = TileGeo<D>;
+  constexpr int RPI = 64 / G::CPR;
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + lane / G::CPR, c = lane % G::CPR;
+    const int32_t m = m0 + r;
+    old_rows[r0 / RPI] = m < mend ? *reinterpret_cast<const uint4 *>(base + (uint32_t)member_token(geo, m) * D + 8 * c)
+                                  : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -563,6 +582,12 @@ __global__ __launch_bounds__(256, 2) void bwd_small_bf16(BwdLaunch p) {
 
   const bool qrole = wave < 2;
   const int w2 = wave & 1;
+  // The rows this wave adds its dQ (query waves) or dK (key waves) onto, loaded
+  // now so that the load overlaps the whole computation instead of the store.
+  constexpr int kOldRows = 32 * G::CPR / 64;
+  uint4 old_rows[kOldRows];
+  if (p.accumulate != 0)
+    load_old_rows<D>(static_cast<const u16 *>(qrole ? p.dq : p.dk) + slice, geo, 32 * w2, geo.len, lane, old_rows);
   // this lane's own row (a query or a key) of the two register operands, read from its tile
   const unsigned char *own_a = (qrole ? qt : kt) + 32 * w2 * G::ROWB;
   const unsigned char *own_b = (qrole ? dt : vt) + 32 * w2 * G::ROWB;
@@ -656,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void bwd_small_bf16(BwdLaunch p) {
   unsigned char *ot = lds + wave * 32 * (4 * D);
   const int32_t r0 = 32 * w2;
   store_rows_lds<D>(ot, acc_a, p.scale, col, half, lane,
-                    static_cast<u16 *>(qrole ? p.dq : p.dk) + slice, geo, r0, geo.len, p.accumulate != 0);
+                    static_cast<u16 *>(qrole ? p.dq : p.dk) + slice, geo, r0, geo.len, p.accumulate != 0, old_rows);
   __syncthreads();
   if (!qrole)
     store_rows_lds<D>(ot, acc_b, 1.f, col, half, lane, static_cast<u16 *>(p.dv) + slice, geo, r0, geo.len, false);
