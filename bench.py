@@ -337,6 +337,9 @@ def main():
         ma.monarch_attn_fwd(q, k, v, o, ws, T, H, W)
         ms_bwd = time_loop(lambda i: ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W),
                            max(3, args.steps // 4), 2)
+        y_fwd = ws[:q.numel()].view(q.shape)   # the forward's Y, kept as a training step would
+        ms_bwd_y = time_loop(lambda i: ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W, y=y_fwd),
+                             max(3, args.steps // 4), 2)
         del grads, wsb, dout
         bwd_flops = 2.5 * (fr + fl)
         fr3, br3 = stage_work(N, d, heads, W)
@@ -355,6 +358,7 @@ def main():
             "chunk_step_t18_ms": round(ms_step, 4),
             "chunk_step_t18_roofline_frac": round(roof_step / (ms_step * 1e3), 4),
             "backward_ms": round(ms_bwd, 4),
+            "backward_saved_y_ms": round(ms_bwd_y, 4),
             # algorithmic work of a backward, counted as FlashAttention does: 2.5x the forward's
             # matmul flops (five products against two); the kernels also recompute Y and P
             "backward_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 1),

@@ -160,16 +160,21 @@ int ma_stage_l_fwd(const void *q, const void *k, const void *y, void *out,
  *     dQ_G = s dS K_G,  dK_G = s dS^T Q_G;
  *   stage L (V := Y, O := out) gives dQ_L, dK_L and dY; stage R (O := Y,
  *   dO := dY) gives dQ_R, dK_R and dV; dq = dQ_L + dQ_R, dk = dK_L + dK_R.
- * out must be the forward output (it enters D). The workspace (at least
- * ma_bwd_workspace_bytes(...) bytes) holds the recomputed Y, dY and per-query
- * softmax statistics; it must not overlap any tensor argument, and dq, dk, dv
- * must not overlap each other or the inputs. dtype MA_F32 returns
+ * out must be the forward output (it enters D). y_fwd may be NULL, or the
+ * forward's Y (the contents of monarch_attn_fwd's / monarch_attn_tiled_fwd's
+ * workspace after that call, same shape and dtype as q; read only, 16-byte
+ * aligned, not overlapping the workspace or dq, dk, dv): given, the backward
+ * takes it instead of recomputing stage R (ignored when a stage is the
+ * identity); the gradients are the same bits either way. The workspace (at
+ * least ma_bwd_workspace_bytes(...) bytes) holds the recomputed Y, dY and
+ * per-query softmax statistics; it must not overlap any tensor argument, and
+ * dq, dk, dv must not overlap each other or the inputs. dtype MA_F32 returns
  * MA_ERR_UNSUPPORTED; ma_bwd_workspace_bytes then returns 0. */
 size_t ma_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
                               int32_t r_axes, int32_t tile_t, int32_t tile_h,
                               int32_t head_dim, int32_t dtype);
 int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *out,
-                     const void *dout, void *dq, void *dk, void *dv,
+                     const void *dout, const void *y_fwd, void *dq, void *dk, void *dv,
                      void *workspace, size_t workspace_bytes,
                      int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
                      int32_t r_axes, int32_t tile_t, int32_t tile_h,

@@ -38,7 +38,7 @@ SIGNATURES = {
     "ma_stage_r_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 8 + [_PTR]),
     "ma_stage_l_fwd": (ctypes.c_int, [_PTR] * 4 + [_I32] * 10 + [_PTR]),
     "ma_bwd_workspace_bytes": (_SIZE, [_I32] * 10),
-    "monarch_attn_bwd": (ctypes.c_int, [_PTR] * 9 + [_SIZE] + [_I32] * 10 + [_PTR]),
+    "monarch_attn_bwd": (ctypes.c_int, [_PTR] * 10 + [_SIZE] + [_I32] * 10 + [_PTR]),
     "ma_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ma_last_hip_error": (ctypes.c_int, []),
 }
@@ -191,12 +191,15 @@ def ma_bwd_workspace_bytes(batch, heads, T, H, W, r_axes=1, tile_t=0, tile_h=0, 
 
 
 def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, workspace, T, H, W, r_axes=1, tile_t=0,
-                     tile_h=0, stream=None):
-    """dq, dk, dv of the forward (same r_axes / tile) given dout; bf16 only."""
+                     tile_h=0, stream=None, y=None):
+    """dq, dk, dv of the forward (same r_axes / tile) given dout; bf16 only. `y`: the
+    forward's Y (its workspace viewed as q's shape) to skip recomputing stage R, or None."""
     _check(q, k, v, out, dout, dq, dk, dv)
+    if y is not None:
+        _check(q, y)
     B, h, N, d = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("monarch_attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk),
-          _ptr(dv), _ptr(workspace), ws_bytes, B, h, T, H, W, r_axes, tile_t, tile_h, d,
+    _call("monarch_attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(y), _ptr(dq),
+          _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, h, T, H, W, r_axes, tile_t, tile_h, d,
           _dtype_code(q), _stream_ptr(q, stream))
     return dq, dk, dv

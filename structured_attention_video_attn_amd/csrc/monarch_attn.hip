@@ -514,7 +514,7 @@ size_t ma_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t T, int32_t H
 }
 
 int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
-                     void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                     const void *y_fwd, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
                      int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W, int32_t r_axes,
                      int32_t tile_t, int32_t tile_h, int32_t head_dim, int32_t dtype,
                      struct ihipStream_t *stream) {
@@ -548,6 +548,14 @@ int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *ou
     if (ranges_overlap(workspace, need, x, tb)) return MA_ERR_INVALID_ARG;
   for (const void *x : outs)
     if (ranges_overlap(workspace, need, x, tb)) return MA_ERR_INVALID_ARG;
+  // the forward's Y, when the caller kept it (read only): used only when both stages run
+  const bool have_y = y_fwd != nullptr && !p.r_trivial && !p.l_trivial;
+  if (have_y) {
+    if (!aligned16(y_fwd)) return MA_ERR_ALIGNMENT;
+    if (ranges_overlap(workspace, need, y_fwd, tb)) return MA_ERR_INVALID_ARG;
+    for (const void *x : outs)
+      if (overlaps(x, y_fwd, tb)) return MA_ERR_INVALID_ARG;
+  }
 
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   void *y = ws;
@@ -559,9 +567,12 @@ int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *ou
     // stage L is the identity: O = Y and dY = dO, and stage R alone writes dq and dk
     return run_stage_bwd(p, gr, q, k, v, out, dout, dq, dk, dv, st_r, false, stream);
   }
-  // Y = stage R of the forward, recomputed (V itself when stage R is the identity)
+  // Y = stage R of the forward: the caller's copy, or recomputed into the
+  // workspace (V itself when stage R is the identity)
   const void *yv = v;
-  if (!p.r_trivial) {
+  if (have_y) {
+    yv = y_fwd;
+  } else if (!p.r_trivial) {
     Plan pr{};
     st = plan_launch(p, gr, q, k, v, y, &pr);
     if (st == MA_OK) st = run_plan(p, pr, stream);
@@ -573,7 +584,7 @@ int monarch_attn_bwd(const void *q, const void *k, const void *v, const void *ou
   st = run_stage_bwd(p, gl, q, k, yv, out, dout, dq, dk, p.r_trivial ? dv : dy, st_l, false, stream);
   if (st != MA_OK || p.r_trivial) return st;
   // stage R, fed dY: dQ_R and dK_R added to dq and dk; dV
-  return run_stage_bwd(p, gr, q, k, v, y, dy, dq, dk, dv, st_r, true, stream);
+  return run_stage_bwd(p, gr, q, k, v, yv, dy, dq, dk, dv, st_r, true, stream);
 }
 
 const char *ma_status_string(int status) {

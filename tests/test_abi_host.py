@@ -154,12 +154,12 @@ def test_backward_workspace_and_argument_errors(lib):
     assert wsb(1, 12, 21, 30, 52, 1, 0, 0, 48, BF16) == 0      # unsupported head_dim
     assert wsb(0, 12, 21, 30, 52, 1, 0, 0, 128, BF16) == 0     # empty
     f = lib.monarch_attn_bwd
-    q, k, v, o, do, dq, dk, dv, w = _ptrs(9)
+    q, k, v, o, do, dq, dk, dv, w, y = _ptrs(10)
     nb = wsb(1, 12, 21, 30, 52, 1, 0, 0, 128, BF16)
 
-    def call(q=q, k=k, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv, w=w, wb=nb, r=1, tt=0, th=0, d=128, dt=BF16,
-             batch=1):
-        return f(q, k, v, o, do, dq, dk, dv, w, wb, batch, 12, 21, 30, 52, r, tt, th, d, dt, None)
+    def call(q=q, k=k, v=v, o=o, do=do, y=None, dq=dq, dk=dk, dv=dv, w=w, wb=nb, r=1, tt=0, th=0, d=128,
+             dt=BF16, batch=1):
+        return f(q, k, v, o, do, y, dq, dk, dv, w, wb, batch, 12, 21, 30, 52, r, tt, th, d, dt, None)
 
     assert call(dt=F32) == UNSUPPORTED
     assert call(d=48) == UNSUPPORTED
@@ -174,6 +174,10 @@ def test_backward_workspace_and_argument_errors(lib):
     assert call(w=do + 4096) == INVALID             # workspace starts inside dout
     assert call(w=A16 + 9 * BIG, k=A16 + 9 * BIG + nb - 16) == INVALID   # k starts inside the workspace
     assert call(r=2, tt=3, th=30) == INVALID        # tiles need r_axes 1
+    assert call(y=y + 4) == ALIGN                   # the forward's Y, misaligned
+    assert call(y=w + 4096) == INVALID              # ... inside the workspace
+    assert call(y=dk) == INVALID                    # ... aliasing a gradient
+    assert call(y=y + 4, dt=F32) == UNSUPPORTED     # dtype is checked first
     assert call(q=None, k=None, v=None, o=None, do=None, dq=None, dk=None, dv=None, w=None, batch=0) == OK
 
 

@@ -32,8 +32,9 @@ def _gpu():
     ma.load_library()
 
 
-def run_bwd(q, k, v, do, grid, r_axes=1, tile=None):
-    """Forward then backward through the C ABI; returns (dq, dk, dv) as float64."""
+def run_bwd(q, k, v, do, grid, r_axes=1, tile=None, saved_y=False):
+    """Forward then backward through the C ABI; returns (dq, dk, dv) as float64.
+    saved_y: hand the forward's Y (its workspace) to the backward."""
     import torch
     import structured_attention_video_attn_amd as ma
     T, H, W = grid
@@ -51,7 +52,8 @@ def run_bwd(q, k, v, do, grid, r_axes=1, tile=None):
     grads = [torch.full_like(qd, float("nan")) for _ in range(3)]
     nbw = ma.ma_bwd_workspace_bytes(B, h, T, H, W, r, tt, th, d, ma.MA_BF16)
     wsb = torch.full((nbw // 2,), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ma.monarch_attn_bwd(qd, kd, vd, out, dod, *grads, wsb, T, H, W, r, tt, th)
+    y = ws[:qd.numel()].view(qd.shape) if saved_y and nb > 0 else None
+    ma.monarch_attn_bwd(qd, kd, vd, out, dod, *grads, wsb, T, H, W, r, tt, th, y=y)
     torch.cuda.synchronize()
     return tuple(download(g) for g in grads)
 
@@ -91,6 +93,17 @@ def test_backward_small(grid, r_axes, tile, d):
     check(got, ref, "bwd %s r=%d tile=%s d=%d" % (grid, r_axes, tile, d))
 
 
+@pytest.mark.parametrize("d", [128, 32])
+@pytest.mark.parametrize("grid,r_axes,tile", SMALL)
+def test_backward_saved_y_same_bits(grid, r_axes, tile, d):
+    # the forward's Y handed to the backward replaces the recomputed one bit for bit
+    q, k, v, do = _randn(grid, 2, d, seed=600 + d)
+    fresh = run_bwd(q, k, v, do, grid, r_axes, tile)
+    saved = run_bwd(q, k, v, do, grid, r_axes, tile, saved_y=True)
+    for name, a, b in zip(("dq", "dk", "dv"), fresh, saved):
+        assert np.array_equal(a, b), "%s differs with the saved Y (%s r=%d tile=%s d=%d)" % (name, grid, r_axes, tile, d)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["chunk", "chunk_sharp"])
 def test_backward_chunk(name):
@@ -101,8 +114,9 @@ def test_backward_chunk(name):
     check(run_bwd(q, k, v, do, grid), mb.monarch_attention_backward(q, k, v, do, grid), name + " bwd")
     # (3, 10) boxes: three per stage-L group at this 3-frame grid (the workload's own 3 x 30
     # tile spans whole groups here, where tiled and untiled coincide)
-    check(run_bwd(q, k, v, do, grid, 1, (3, 10)), mb.monarch_attention_backward(q, k, v, do, grid, tile=(3, 10)),
-          name + " bwd tiled (3, 10)")
+    ref_tiled = mb.monarch_attention_backward(q, k, v, do, grid, tile=(3, 10))
+    check(run_bwd(q, k, v, do, grid, 1, (3, 10)), ref_tiled, name + " bwd tiled (3, 10)")
+    check(run_bwd(q, k, v, do, grid, 1, (3, 10), saved_y=True), ref_tiled, name + " bwd tiled (3, 10), saved Y")
 
 
 @pytest.mark.timeout(900)
