@@ -166,6 +166,35 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, ker
     print(json.dumps(out))
 
 
+def measured_peaks(dev):
+    """What this machine delivers to plain library calls, beside the vendor peaks: a
+    device-to-device copy (read + write) and a bf16 GEMM through torch (hipBLASLt)."""
+    import torch
+    def timed(fn, iters):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters * 1e-3
+    src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    copy_gbps = 2.0 * src.numel() * 2 / t_copy / 1e9
+    del src, dst
+    n = 8192
+    gen = torch.Generator(device=dev).manual_seed(11)
+    x = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=gen)
+    w = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=gen)
+    t_mm = timed(lambda: torch.mm(x, w), 10)
+    return {"device_copy_GBps": round(copy_gbps, 1),
+            "torch_mm_bf16_8192_TFLOPs": round(2.0 * n ** 3 / t_mm / 1e12, 1)}
+
+
 def profile_only(which, steps, warmup=0, n_sets=3):
     """Run one kernel `steps` times over rotating buffer sets (about 1.5 GB in all,
     more than the 256 MB MALL), so that every launch reads its inputs from HBM; the
@@ -253,7 +282,10 @@ def main():
     ms = time_loop(step, args.steps, args.warmup)
     ms_warm = time_loop(lambda i: step(0), args.steps, args.warmup)
 
-    # Per-kernel durations, live, with events on the stream the kernels run on.
+    # Per-kernel durations, live, with events on the stream the kernels run on,
+    # each launch bracketed inside the step it belongs to: stage L reads the Y that
+    # stage R has just written, as in monarch_attn_fwd (launched back to back over
+    # the rotating sets instead, stage L reads Y cold and takes ~8% longer).
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.warmup):
@@ -274,6 +306,7 @@ def main():
     fr, br = stage_work(N, d, heads, W)
     fl, bl = stage_work(N, d, heads, T * H)
     roof_r, roof_l = roofline_us(fr, br), roofline_us(fl, bl)
+    roof_min = roofline_us(fr + fl, 8.0 * N * d * heads)
     if l_us >= r_us:
         name, dur, f, b = "stage_l", l_us, fl, bl
     else:
@@ -366,6 +399,7 @@ def main():
             "dense_ms": round(ms_dense, 3),
             "dense_tflops": round(4.0 * N * N * d * heads / (ms_dense * 1e-3) / 1e12, 1),
             "monarch_speedup_vs_dense": round(ms_dense / ms, 2),
+            "measured_peaks": measured_peaks(dev),
         }
 
     out = {
@@ -388,6 +422,10 @@ def main():
         "roofline": roofline,
         "step_roofline": {"roofline_us": round(roof_r + roof_l, 2), "measured_us": round(ms * 1e3, 2),
                           "frac": round((roof_r + roof_l) / (ms * 1e3), 4),
+                          # the method's own minimum: Q, K, V read and O written once
+                          # (Y never leaves the chip), all products at peak
+                          "method_min_us": round(roof_min, 2),
+                          "frac_method_min": round(roof_min / (ms * 1e3), 4),
                           "stage_r_us": round(r_us, 2), "stage_l_us": round(l_us, 2)},
         "warm_ms_per_step": round(ms_warm, 5),
     }
