@@ -374,6 +374,23 @@ def main():
         ms_bwd_y = time_loop(lambda i: ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W, y=y_fwd),
                              max(3, args.steps // 4), 2)
         del grads, wsb, dout
+        # the 81x30x52 workload (126360 tokens, 16 heads, Q, K, V ~ N(0, 1)): untiled and
+        # in 9-frame x 30-row tiles
+        wl4 = WORKLOADS["long"]
+        T4, H4, W4, h4 = wl4.T, wl4.H, wl4.W, wl4.heads
+        N4 = T4 * H4 * W4
+        g4 = torch.Generator(device=dev).manual_seed(wl4.seed)
+        q4, k4, v4 = (torch.randn(1, h4, N4, d, generator=g4, device=dev).to(torch.bfloat16) for _ in range(3))
+        o4, ws4 = torch.empty_like(q4), torch.empty_like(q4)
+        tt4, th4 = wl4.tile
+        n4 = max(3, args.steps // 5)
+        ms_long = time_loop(lambda i: ma.monarch_attn_fwd(q4, k4, v4, o4, ws4, T4, H4, W4), n4, 3)
+        ms_long_tiled = time_loop(lambda i: ma.monarch_attn_tiled_fwd(q4, k4, v4, o4, ws4, T4, H4, W4, tt4, th4),
+                                  n4, 3)
+        del q4, k4, v4, o4, ws4
+        roof_r4 = roofline_us(*stage_work(N4, d, h4, W4))
+        roof_long = roof_r4 + roofline_us(*stage_work(N4, d, h4, T4 * H4))
+        roof_long_tiled = roof_r4 + roofline_us(*stage_work(N4, d, h4, tt4 * th4))
         bwd_flops = 2.5 * (fr + fl)
         fr3, br3 = stage_work(N, d, heads, W)
         fl3, bl3 = stage_work(N, d, heads, tt * th)
@@ -399,6 +416,10 @@ def main():
             "dense_ms": round(ms_dense, 3),
             "dense_tflops": round(4.0 * N * N * d * heads / (ms_dense * 1e-3) / 1e12, 1),
             "monarch_speedup_vs_dense": round(ms_dense / ms, 2),
+            "long_81x30x52_h16_ms": round(ms_long, 4),
+            "long_81x30x52_h16_roofline_frac": round(roof_long / (ms_long * 1e3), 4),
+            "long_tiled_9x30_ms": round(ms_long_tiled, 4),
+            "long_tiled_9x30_roofline_frac": round(roof_long_tiled / (ms_long_tiled * 1e3), 4),
             "measured_peaks": measured_peaks(dev),
         }
 
