@@ -17,9 +17,8 @@
 //                    block's exponentials between the first block's PV MFMAs.
 //   block_attn_bf16  groups of at most 64 tokens (stage R's W-row blocks,
 //                    small tiles): persistent workgroups of 2 waves walk over
-//                    the groups and prefetch the next group's keys, values
-//                    and queries while computing the current one, keeping
-//                    HBM requests in flight at all times.
+//                    the groups, one group at a time; four of them resident
+//                    per CU keep HBM requests in flight while each computes.
 //
 // Data movement. Key and value tiles go global -> LDS by direct-to-LDS DMA
 // (global_load_lds_dwordx4: lane l of an instruction fills LDS bytes

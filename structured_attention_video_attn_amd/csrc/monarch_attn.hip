@@ -148,10 +148,11 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
     q_per_block = kKeyTile;   // one group per work item
     pl->kernel = Kernel::kBlock;
   } else {
-    // Workgroups of up to 4 waves (128 queries), two resident per CU with a
-    // double-buffered ring: measured faster on MI355X than 8-wave workgroups
-    // with a 4-deep ring, whose waves all meet at every barrier together even
-    // though they copy each group's keys and values into LDS fewer times.
+    // Workgroups of up to 4 waves (128 queries), two resident per CU, each with
+    // a ring of three key and two value tiles: measured faster on MI355X than
+    // 8-wave workgroups (a 4-deep ring shared by 256 queries, or two items whose
+    // halves alternate matrix and vector sections), whose waves all meet at
+    // every barrier together.
     // The group's queries are spread evenly over its workgroups; the wave
     // count is the power of two that covers a share and that the DMA split
     // allows (D/8 16-byte chunks per row).
