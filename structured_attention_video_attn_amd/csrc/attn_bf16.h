@@ -255,25 +255,6 @@ __device__ __forceinline__ void attend_tile(const unsigned char *ks, const unsig
                  [](int) {}, [](int) {});
 }
 
-// Normalise and store this lane's query row (O^T element r of d-block b is
-// head_dim 32b + 8(r/4) + 4half + r%4).
-template <int D>
-__device__ __forceinline__ void store_row(u16 *orow, const f32x16_t *oacc, float l_run, int half) {
-  const float inv = 1.f / (l_run + swap_halves(l_run));
-#pragma unroll
-  for (int b = 0; b < TileGeo<D>::DB; ++b)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * b + 8 * rq + 4 * half;
-      if (d0 < D) {
-        bf16x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[b][4 * rq + e] * inv);
-        *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
-      }
-    }
-}
-
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
