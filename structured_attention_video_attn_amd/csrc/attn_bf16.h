@@ -84,21 +84,26 @@ struct TileGeo {
 };
 
 // Position of 16-byte chunk c of tile row r (CPR chunks per row, a power of 2).
-// The LDS serves 256 bytes (64 banks) per cycle. At head_dim 128 a tile row is
-// those 256 bytes, and row 4q + p (p, q < 4, row taken mod 16) gets the mask
-// 4p + q: any 16 consecutive rows get 16 different masks (a 16-byte read of
-// one chunk column serves 16 lanes per cycle, one row each), and the four
-// rows of an aligned quad get masks in four different quarters of the row (an
-// 8-byte transposed read serves 32 lanes per cycle over four rows and one
-// quarter of the chunks each), so neither read meets a bank twice.
+// The LDS serves 256 bytes (64 banks) per cycle: a 16-byte read of one chunk
+// column serves 16 lanes, one tile row each, and an 8-byte transposed value
+// read serves 32 lanes over four consecutive rows and a quarter of the
+// columns each. Row r gets an XOR mask that depends on r mod 16 only, chosen
+// so that neither read meets a bank twice (rows of 256 bytes fill a bank line
+// at head_dim 128; at 64, 32 and 16 two, four and eight rows share one):
+//   D = 128: row 4q + p gets 4p + q;      D = 64: bit 1 of r -> bit 2, bits 2-3 -> bits 0-1;
+//   D = 32:  bits 2-3 of r;               D = 16: bit 3 of r.
 template <int CPR>
 __device__ __forceinline__ int swizzle_chunk(int r, int c) {
   if constexpr (CPR == 16) {
     return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else if constexpr (CPR == 8) {
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  } else if constexpr (CPR == 4) {
+    return c ^ ((r >> 2) & 3);
+  } else if constexpr (CPR == 2) {
+    return c ^ ((r >> 3) & 1);
   } else {
-    constexpr int kBits = CPR >= 2 ? __builtin_ctz(CPR) : 0;
-    const int s = ((r << 1) | ((r >> (kBits > 0 ? kBits - 1 : 0)) & 1)) & (CPR - 1);
-    return c ^ s;
+    return c;
   }
 }
 
@@ -361,7 +366,7 @@ __device__ __forceinline__ void exp_pair(const f32x16_t &s, int r, float scale_l
 // Per-lane LDS byte offsets of the streaming tile's fragment reads, relative
 // to the tile buffer: computed once per kernel, so that each read is one
 // ds_read with the buffer (and row-block) base in its immediate offset. The
-// XOR swizzle of row r depends only on r mod (D/8), so value rows
+// XOR swizzle of row r depends only on r mod 16, so value rows
 // 32kb + 16h + tr_key (+8) share the offsets of rows tr_key (+8).
 template <int D>
 struct LaneOffsets {
@@ -413,7 +418,7 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
   constexpr int AK = DK < 2 ? DK : 2;   // k-steps of key fragments in flight
   bf16x8_t kf0[DK], kf1[DK];
   auto read_k = [&](int j) __attribute__((always_inline)) {
-    // rows col and 32 + col share the swizzle (32 is a multiple of D/8)
+    // rows col and 32 + col share the swizzle (it depends on the row mod 16)
     kf0[j] = *reinterpret_cast<const bf16x8_t *>(ks + lo.k[j]);
     kf1[j] = *reinterpret_cast<const bf16x8_t *>(ks + 32 * G::ROWB + lo.k[j]);
   };
