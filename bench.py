@@ -392,6 +392,9 @@ def main():
         roof_long = roof_r4 + roofline_us(*stage_work(N4, d, h4, T4 * H4))
         roof_long_tiled = roof_r4 + roofline_us(*stage_work(N4, d, h4, tt4 * th4))
         bwd_flops = 2.5 * (fr + fl)
+        mp = measured_peaks(dev)
+        roof_m = lambda f_, b_: max(f_ / (mp["torch_mm_bf16_8192_TFLOPs"] * 1e12),
+                                    b_ / (mp["device_copy_GBps"] * 1e9)) * 1e6
         fr3, br3 = stage_work(N, d, heads, W)
         fl3, bl3 = stage_work(N, d, heads, tt * th)
         extras = {
@@ -420,7 +423,12 @@ def main():
             "long_81x30x52_h16_roofline_frac": round(roof_long / (ms_long * 1e3), 4),
             "long_tiled_9x30_ms": round(ms_long_tiled, 4),
             "long_tiled_9x30_roofline_frac": round(roof_long_tiled / (ms_long_tiled * 1e3), 4),
-            "measured_peaks": measured_peaks(dev),
+            "measured_peaks": mp,
+            # the same rooflines with this box's measured copy and GEMM rates as the peaks
+            "step_roofline_frac_measured_peaks": round(
+                (roof_m(fr, br) + roof_m(fl, bl)) / (ms * 1e3), 4),
+            "tiled_structured_roofline_frac_measured_peaks": round(
+                (roof_m(fr3, br3) + roof_m(fl3, bl3)) / (ms_tiled * 1e3), 4),
         }
 
     out = {
