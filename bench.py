@@ -138,9 +138,10 @@ def _counter_rows(d, counter):
     return rows
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel):
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, out_path=None):
     """Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    each scaled by what the same counter reads for a device copy of one 100.6 MB tensor."""
+    each scaled by what the same counter reads for a device copy of one 100.6 MB tensor;
+    written to out_path (default profiles/traffic_full_<kernel>.json) and returned."""
     wl_bytes = 12 * 32760 * 128 * 2
     sym = KERNEL_SYMBOL[kernel]
 
@@ -160,10 +161,11 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, ker
            "fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write,
            "fetch_scale": fetch_scale, "write_scale": write_scale,
            "algorithmic_bytes": 8.0 * 32760 * 128 * 12}
-    path = os.path.join(ROOT, "profiles", "traffic_full_%s.json" % kernel)
+    path = out_path or os.path.join(ROOT, "profiles", "traffic_full_%s.json" % kernel)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
+    return out
 
 
 def measured_peaks(dev):
@@ -246,7 +248,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the method is measured on a single MI355X and "
-              "this build has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+              "the library has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

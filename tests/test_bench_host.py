@@ -1,0 +1,62 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU guard, the roofline arithmetic of the
+21x30x52, 12-head, d128 workload, and the counter summary's copy calibration on synthetic
+rocprofv3 csv output."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+
+
+def test_roofline_arithmetic():
+    N, d, h = 32760, 128, 12
+    fr, br = bench.stage_work(N, d, h, 52)     # stage R: blocks of W = 52
+    fl, bl = bench.stage_work(N, d, h, 630)    # stage L: groups of T*H = 630
+    assert br == bl == 8 * N * d * h == 402554880
+    assert fr == 4.0 * N * d * h * 52 and fl == 4.0 * N * d * h * 630
+    # stage R is HBM-bound (50.32 us at 8 TB/s), stage L MFMA-bound (50.72 us at 2.5 PF)
+    assert bench.roofline_us(fr, br) == pytest.approx(br / 8e12 * 1e6)
+    assert bench.roofline_us(fl, bl) == pytest.approx(fl / 2.5e15 * 1e6)
+    assert bench.roofline_us(fr, br) + bench.roofline_us(fl, bl) == pytest.approx(101.04, abs=0.01)
+
+
+def _write_counters(d, rows):
+    os.makedirs(d)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(["Kernel_Name", "Counter_Name", "Counter_Value"], r)))
+
+
+def test_counter_summary_scales_by_the_copy(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    kern = "void ma::group_attn_bf16<128, 4, false>(ma::AttnLaunch)"
+    # a copy of one 100.6 MB tensor reads FETCH 49140 KiB and WRITE 98280 KiB per dispatch
+    _write_counters(str(tmp_path / "cf"), [(copy, "FETCH_SIZE", 49140)] * 3 + [(kern, "FETCH_SIZE", 1)])
+    _write_counters(str(tmp_path / "cw"), [(copy, "WRITE_SIZE", 98280)] * 3)
+    _write_counters(str(tmp_path / "kf"), [(kern, "FETCH_SIZE", 150000), (kern, "FETCH_SIZE", 150002),
+                                           ("other", "FETCH_SIZE", 7)])
+    _write_counters(str(tmp_path / "kw"), [(kern, "WRITE_SIZE", 98280)] * 2)
+    out = bench.summarize_counters(str(tmp_path / "kf"), str(tmp_path / "kw"), str(tmp_path / "cf"),
+                                   str(tmp_path / "cw"), "stage_l", out_path=str(tmp_path / "t.json"))
+    tensor = 12 * 32760 * 128 * 2
+    assert out["fetch_scale"] == pytest.approx(tensor / (1024.0 * 49140))
+    assert out["write_scale"] == pytest.approx(tensor / (1024.0 * 98280))
+    assert out["fetch_bytes"] == pytest.approx(1024.0 * 150001 * out["fetch_scale"])
+    assert out["write_bytes"] == pytest.approx(1024.0 * 98280 * out["write_scale"])
+    assert out["bytes_per_launch"] == pytest.approx(out["fetch_bytes"] + out["write_bytes"])
+    assert out["algorithmic_bytes"] == 8.0 * 32760 * 128 * 12
+    assert os.path.exists(str(tmp_path / "t.json"))
