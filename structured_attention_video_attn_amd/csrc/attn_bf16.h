@@ -514,21 +514,51 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   unsigned char *const yt0 = lds, *const yt1 = lds + G::TILEB;
   unsigned char *const kt0 = lds + 2 * G::TILEB, *const kt1 = lds + 3 * G::TILEB, *const kt2 = lds + 4 * G::TILEB;
 
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const bool packed = p.span_waves > 0;
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
   const uint32_t rest0 = bid / (uint32_t)p.n_qtiles;
-  const int32_t span = (int32_t)(rest0 % (uint32_t)p.n_spans);
-  const uint32_t rest = rest0 / (uint32_t)p.n_spans;
+  const int32_t span = packed ? 0 : (int32_t)(rest0 % (uint32_t)p.n_spans);
+  const uint32_t rest = packed ? rest0 : rest0 / (uint32_t)p.n_spans;
   const int32_t g = (int32_t)(rest % (uint32_t)p.ga.n_groups);
   const int64_t bh = (int64_t)(rest / (uint32_t)p.ga.n_groups);
   const GroupGeom geo = group_geom(p.ga, g);
-  // queries [span_lo, span_hi) of the group; keys [0, klen)
-  const int32_t span_lo = p.q_first + span * p.q_span;
-  const int32_t span_hi = p.q_span > 0 ? min(geo.len, span_lo + p.q_span) : geo.len;
-  const int32_t klen = span_hi;
-  const int32_t qbase = span_lo + qt * p.q_tile;
-  if (qbase >= span_hi) return;   // uniform over the workgroup
-  const int32_t qend = min(span_hi, qbase + p.q_tile);
+  // This wave's queries [q0, min(q0 + 32, qhi)) attend to keys [0, qhi)
+  // (qhi = 0: no queries); the workgroup streams keys [0, klen).
+  int32_t q0, qhi, klen;
+  if (packed) {
+    // wave item i (of the group's items, in span order from the last span
+    // down): span s, wave j of that span
+    auto item_range = [&](int32_t i, int32_t &lo, int32_t &hi) __attribute__((always_inline)) {
+      int32_t s, j;
+      if (i < p.last_waves) {
+        s = p.n_spans - 1;
+        j = i;
+      } else {
+        const int32_t i2 = i - p.last_waves;
+        s = p.n_spans - 2 - i2 / p.span_waves;
+        j = i2 % p.span_waves;
+      }
+      const int32_t base = p.q_first + s * p.q_span;
+      lo = s >= 0 ? base + kQueriesPerWave * j : p.q_first;
+      hi = s >= 0 ? min(geo.len, base + p.q_span) : 0;
+    };
+    int32_t lo0;
+    item_range(qt * NW, lo0, klen);   // the workgroup's first item has the longest span
+    item_range(qt * NW + wave, q0, qhi);
+  } else {
+    // queries [span_lo, span_hi) of the group, this workgroup's q_tile of them
+    const int32_t span_lo = p.q_first + span * p.q_span;
+    const int32_t span_hi = p.q_span > 0 ? min(geo.len, span_lo + p.q_span) : geo.len;
+    const int32_t qbase = span_lo + qt * p.q_tile;
+    const int32_t qend = min(span_hi, qbase + p.q_tile);
+    q0 = qbase + kQueriesPerWave * wave;
+    qhi = q0 < qend ? span_hi : 0;
+    klen = qbase < span_hi ? span_hi : 0;
+  }
+  if (klen == 0) return;   // uniform over the workgroup
   const RowMap rm = row_map(geo);
 
   const unsigned char *qbytes = uniform_ptr(
@@ -538,8 +568,6 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   const unsigned char *vbytes = uniform_ptr(
       reinterpret_cast<const unsigned char *>(static_cast<const u16 *>(p.vals) + bh * p.head_elems));
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int tr_key = 4 * half + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -574,20 +602,33 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
 
   const LaneOffsets<D> lo = lane_offsets<D>(col, half, tr_key, tr_col);
 
-  const int32_t q0 = qbase + wave * kQueriesPerWave;
-  const int32_t qm = q0 + col;
-  const bool wave_active = q0 < qend;   // wave-uniform
-
   const int32_t n = (klen + kKeyTile - 1) / kKeyTile;
+  const int32_t wave_n = q0 < qhi ? (qhi + kKeyTile - 1) / kKeyTile : 0;   // tiles this wave computes
   // Prologue. The workgroup's 32*NW query rows come in like key tiles (whole
   // rows per DMA window, rather than 16 bytes of 64 rows per load) into the
   // buffers of value tile 1 and key tile 2, which stay free until step 0
-  // refills them; then K(0), Y(0), K(1).
+  // refills them; then K(0), Y(0), K(1). Each wave loads its own 32 rows
+  // (queries need not be contiguous across waves): the windows of buffer
+  // rows 32*(wave % 2) .. +31, as many windows as WPT per tile of NW waves.
+  {
+    constexpr int QW = kQueriesPerWave / G0::ROWS_PER_INST;
+    static_assert(QW == (NW > 2 ? 2 : 1) * WPT, "query windows: the count the vmcnt waits assume");
+    unsigned char *qdst = wave < 2 ? yt1 : kt2;
+    const int32_t qk0 = q0 - kQueriesPerWave * (wave & 1);
 #pragma unroll
-  for (int w = 0; w < WPT; ++w) window(qbytes, yt1, qbase, w);
-  if constexpr (NW > 2) {
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) window(qbytes, kt2, qbase + kKeyTile, w);
+    for (int i = 0; i < QW; ++i) {
+      const int ii = (wave & 1) * QW + i;
+      if constexpr (kTwoLevel) {
+        dma_row_window<D>(qbytes, qdst, rm, qk0, ii, lane);
+      } else {
+        const int r = ii * G0::ROWS_PER_INST + lane_row;
+        const int32_t km = min(qk0 + r, rm.last);
+        dma16(qbytes,
+              __umul24((uint32_t)km, mstride) + (uint32_t)rm.base * (2u * D) +
+                  16u * (uint32_t)swizzle_chunk<G0::CPR>(r, lane % G0::CPR),
+              qdst + ii * 1024);
+      }
+    }
   }
 #pragma unroll
   for (int w = 0; w < WPT; ++w) window(kbytes, kt0, 0, w);
@@ -625,7 +666,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
     wait_vmcnt<WPT>();
     __syncthreads();   // tile t visible; buffers of tiles t-1 (values) and t-1 (keys) free
     const int32_t yk0 = (t + 1) * kKeyTile, kk0 = (t + 2) * kKeyTile;
-    if (wave_active) {
+    if (t < wave_n) {
       // value windows of tile t+1 precede the key windows of tile t+2 in issue order
 #pragma unroll
       for (int w = XQ; w < WPT; ++w) window(vbytes, yn, yk0, w);
@@ -635,7 +676,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
       auto on_pv = [&](int i) __attribute__((always_inline)) {
         if (i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
-      stream_tile<D>(kc, yc, qb, t * kKeyTile, klen, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
+      stream_tile<D>(kc, yc, qb, t * kKeyTile, qhi, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
                      on_qk, on_pv);
 #pragma unroll
       for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);
@@ -692,7 +733,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
     const int r = r0 + lane / G::CPR, c = lane % G::CPR;
     const uint4 v = *reinterpret_cast<const uint4 *>(ot + r * G::ROWB + 16 * (c ^ (r & (G::CPR - 1))));
     const int32_t m = q0 + r;
-    if (m < qend) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(geo, m) * D + 8 * c) = v;
+    if (m < qhi) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(geo, m) * D + 8 * c) = v;
   }
 }
 

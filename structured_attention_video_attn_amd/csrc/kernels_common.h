@@ -25,6 +25,12 @@ struct AttnLaunch {
   int32_t q_first;
   int32_t q_span;
   int32_t n_spans;
+  // span_waves > 0 (several spans): spans are cut into wave items of 32
+  // queries (span_waves per span, last_waves in the last one), ordered by
+  // span from the last to the first, and workgroup qt of a group runs items
+  // qt*NW .. qt*NW+NW-1, one per wave; n_qtiles counts those workgroups.
+  int32_t span_waves;
+  int32_t last_waves;
   int32_t n_bh;       // batch * heads
   float scale;        // 1/sqrt(head_dim)
   float scale_log2;   // scale * log2(e): softmax evaluated with exp2

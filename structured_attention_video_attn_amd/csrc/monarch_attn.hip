@@ -170,8 +170,22 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
   }
   a.n_qtiles = (qlen + q_per_block - 1) / q_per_block;
   a.q_tile = q_per_block;
-  const uint64_t blocks =
-      (uint64_t)a.n_qtiles * (uint64_t)a.n_spans * (uint64_t)ga.n_groups * (uint64_t)a.n_bh;
+  uint64_t per_group = (uint64_t)a.n_qtiles * (uint64_t)a.n_spans;
+  if (pl->kernel == Kernel::kStream && a.n_spans > 1) {
+    // Several spans: workgroups of full width take wave items (32 queries of
+    // one span) from the longest span down, so a workgroup's waves stream
+    // about as many keys as each other and no wave slot idles for want of
+    // queries (a span rarely fills a whole workgroup).
+    pl->waves = p.D >= 32 ? 4 : 2;
+    a.span_waves = (a.q_span + kQueriesPerWave - 1) / kQueriesPerWave;
+    const int32_t last = queries - (a.n_spans - 1) * a.q_span;
+    a.last_waves = (last + kQueriesPerWave - 1) / kQueriesPerWave;
+    const int64_t items = (int64_t)a.last_waves + (int64_t)(a.n_spans - 1) * a.span_waves;
+    a.n_qtiles = (int32_t)((items + pl->waves - 1) / pl->waves);
+    a.q_tile = kQueriesPerWave * pl->waves;
+    per_group = (uint64_t)a.n_qtiles;
+  }
+  const uint64_t blocks = per_group * (uint64_t)ga.n_groups * (uint64_t)a.n_bh;
   if (blocks > (uint64_t)INT32_MAX) return MA_ERR_UNSUPPORTED;
   pl->blocks = (uint32_t)blocks;
   pl->n_items = (int32_t)blocks;
