@@ -52,6 +52,8 @@
 // tile's max exceeds it by more than 8 (log2 units), so unnormalised weights
 // stay below 2^8 and the result is unchanged up to rounding.
 #pragma once
+#include <type_traits>
+
 #include "kernels_common.h"
 
 namespace ma {
@@ -660,46 +662,59 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   constexpr int XQ = NQ / SQ < WPT ? NQ / SQ : WPT, XP = NP / SP < WPT ? NP / SP : WPT;   // windows in hooks
 
   // One tile: computes from (kc, yc) and fills (yn, kn).
-  auto step = [&](int32_t t, const unsigned char *kc, const unsigned char *yc, unsigned char *yn,
+  // One tile: computes from (kc, yc) and, with DMA, fills (yn, kn). The last
+  // tile runs without DMA: tiles n and n+1 would lie past the group.
+  auto step = [&](auto dma, int32_t t, const unsigned char *kc, const unsigned char *yc, unsigned char *yn,
                   unsigned char *kn) __attribute__((always_inline)) {
+    constexpr bool kDma = decltype(dma)::value;
     // Outstanding: ... Y(t), K(t+1); tile t needs everything but K(t+1).
     wait_vmcnt<WPT>();
     __syncthreads();   // tile t visible; buffers of tiles t-1 (values) and t-1 (keys) free
     const int32_t yk0 = (t + 1) * kKeyTile, kk0 = (t + 2) * kKeyTile;
     if (t < wave_n) {
       // value windows of tile t+1 precede the key windows of tile t+2 in issue order
+      if constexpr (kDma) {
 #pragma unroll
-      for (int w = XQ; w < WPT; ++w) window(vbytes, yn, yk0, w);
+        for (int w = XQ; w < WPT; ++w) window(vbytes, yn, yk0, w);
+      }
       auto on_qk = [&](int i) __attribute__((always_inline)) {
-        if (i % SQ == 0 && i / SQ < XQ) window(vbytes, yn, yk0, (i / SQ));
+        if (kDma && i % SQ == 0 && i / SQ < XQ) window(vbytes, yn, yk0, (i / SQ));
       };
       auto on_pv = [&](int i) __attribute__((always_inline)) {
-        if (i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
+        if (kDma && i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
       stream_tile<D>(kc, yc, qb, t * kKeyTile, qhi, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
                      on_qk, on_pv);
+      if constexpr (kDma) {
 #pragma unroll
-      for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);
-    } else {
+        for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);
+      }
+    } else if constexpr (kDma) {
 #pragma unroll
       for (int w = 0; w < WPT; ++w) window(vbytes, yn, yk0, w);
 #pragma unroll
       for (int w = 0; w < WPT; ++w) window(kbytes, kn, kk0, w);
     }
   };
+  const std::true_type with_dma{};
   // tile t: keys in kt[t % 3], values in yt[t % 2]; fills yt[(t+1) % 2], kt[(t+2) % 3]
-  for (int32_t t = 0; t < n; t += 6) {
-    step(t, kt0, yt0, yt1, kt2);
-    if (t + 1 >= n) break;
-    step(t + 1, kt1, yt1, yt0, kt0);
-    if (t + 2 >= n) break;
-    step(t + 2, kt2, yt0, yt1, kt1);
-    if (t + 3 >= n) break;
-    step(t + 3, kt0, yt1, yt0, kt2);
-    if (t + 4 >= n) break;
-    step(t + 4, kt1, yt0, yt1, kt0);
-    if (t + 5 >= n) break;
-    step(t + 5, kt2, yt1, yt0, kt1);
+  const int32_t nd = n - 1;   // tiles run with DMA
+  for (int32_t t = 0; t < nd; t += 6) {
+    step(with_dma, t, kt0, yt0, yt1, kt2);
+    if (t + 1 >= nd) break;
+    step(with_dma, t + 1, kt1, yt1, yt0, kt0);
+    if (t + 2 >= nd) break;
+    step(with_dma, t + 2, kt2, yt0, yt1, kt1);
+    if (t + 3 >= nd) break;
+    step(with_dma, t + 3, kt0, yt1, yt0, kt2);
+    if (t + 4 >= nd) break;
+    step(with_dma, t + 4, kt1, yt0, yt1, kt0);
+    if (t + 5 >= nd) break;
+    step(with_dma, t + 5, kt2, yt1, yt0, kt1);
+  }
+  {
+    const int r3 = nd % 3;
+    step(std::false_type{}, nd, r3 == 0 ? kt0 : r3 == 1 ? kt1 : kt2, (nd & 1) ? yt1 : yt0, nullptr, nullptr);
   }
   // DMAs into buffers past the last tile may still be in flight; they must
   // land before the buffers are reused below (and before the workgroup's LDS
