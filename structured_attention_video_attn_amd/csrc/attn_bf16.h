@@ -9,12 +9,14 @@
 // on-chip memory).
 //
 //   group_attn_bf16  groups longer than 64 tokens (stage L, long stage-R
-//                    blocks, dense): a workgroup of 4 waves owns 128 queries
-//                    of one group and streams the group's keys and values
-//                    through LDS in 64-row tiles with an online softmax; each
-//                    tile runs in a fixed instruction order that keeps LDS
-//                    reads ahead of the MFMAs and puts the second 32-key
-//                    block's exponentials between the first block's PV MFMAs.
+//                    blocks, dense): a workgroup of 4 waves owns up to 128
+//                    queries of one group, 32 per wave (under chunk-causal
+//                    spans each wave's 32 come from one span), and streams the
+//                    group's keys and values through LDS in 64-row tiles with
+//                    an online softmax; each tile runs in a fixed instruction
+//                    order that keeps LDS reads ahead of the MFMAs and puts the
+//                    second 32-key block's exponentials between the first
+//                    block's PV MFMAs.
 //   block_attn_bf16  groups of at most 64 tokens (stage R's W-row blocks,
 //                    small tiles): persistent workgroups of 2 waves walk over
 //                    the groups, one group at a time; four of them resident
