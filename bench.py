@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector), TFLOP/s
 METRIC = "Monarch-attn ms/call & tokens/s at 21×30×52 grid, 12h d128; % HBM/MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_%s.json")
 KERNEL_SOURCES = ["attn_bf16.h", "group_addr.h", "kernels_common.h", "monarch_attn.hip"]
@@ -393,6 +394,27 @@ def main():
         roof_r4 = roofline_us(*stage_work(N4, d, h4, W4))
         roof_long = roof_r4 + roofline_us(*stage_work(N4, d, h4, T4 * H4))
         roof_long_tiled = roof_r4 + roofline_us(*stage_work(N4, d, h4, tt4 * th4))
+        # fp32 path (fp32 matrix cores at head_dim 128): the 3x30x52 workload and the
+        # full sequence; rooflines at the fp32 peak and 4-byte elements
+        wl1 = WORKLOADS["chunk"]
+        up32 = lambda x: torch.from_numpy(x).to(dev).to(torch.float32)
+        q1, k1, v1 = (up32(x) for x in make_qkv(wl1))
+        o1 = torch.empty_like(q1)
+        ws1 = torch.empty_like(q1)
+        ms_f32_chunk = time_loop(lambda i: ma.monarch_attn_fwd(q1, k1, v1, o1, ws1, wl1.T, wl1.H, wl1.W),
+                                 args.steps, min(args.warmup, 20))
+        del q1, k1, v1, o1, ws1
+        q2, k2, v2 = (up32(x) for x in (q_np, k_np, v_np))
+        o2 = torch.empty_like(q2)
+        ws2 = torch.empty_like(q2)
+        ms_f32_full = time_loop(lambda i: ma.monarch_attn_fwd(q2, k2, v2, o2, ws2, T, H, W),
+                                max(3, args.steps // 10), 3)
+        del q2, k2, v2, o2, ws2
+        roof32 = lambda f_, b_: max(f_ / (PEAK_FP32_TFLOPS * 1e12), 2.0 * b_ / (PEAK_HBM_GBS * 1e9)) * 1e6
+        N1 = wl1.T * wl1.H * wl1.W
+        roof_f32_chunk = (roof32(*stage_work(N1, d, wl1.heads, wl1.W))
+                          + roof32(*stage_work(N1, d, wl1.heads, wl1.T * wl1.H)))
+        roof_f32_full = roof32(fr, br) + roof32(fl, bl)
         bwd_flops = 2.5 * (fr + fl)
         mp = measured_peaks(dev)
         roof_m = lambda f_, b_: max(f_ / (mp["torch_mm_bf16_8192_TFLOPs"] * 1e12),
@@ -418,6 +440,10 @@ def main():
             # matmul flops (five products against two); the kernels also recompute Y and P
             "backward_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 1),
             "backward_mfma_frac": round(bwd_flops / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fp32_chunk_3x30x52_ms": round(ms_f32_chunk, 4),
+            "fp32_chunk_3x30x52_roofline_frac": round(roof_f32_chunk / (ms_f32_chunk * 1e3), 4),
+            "fp32_full_ms": round(ms_f32_full, 4),
+            "fp32_full_roofline_frac": round(roof_f32_full / (ms_f32_full * 1e3), 4),
             "dense_ms": round(ms_dense, 3),
             "dense_tflops": round(4.0 * N * N * d * heads / (ms_dense * 1e-3) / 1e12, 1),
             "monarch_speedup_vs_dense": round(ms_dense / ms, 2),

@@ -23,7 +23,9 @@
  * aligned. The library allocates nothing, keeps no state between calls, and is
  * reentrant; work is enqueued on `stream` (NULL = the default stream) and every
  * call returns without synchronizing. bf16 inputs are accumulated in fp32; the
- * stage-R intermediate Y is stored in the input dtype.
+ * stage-R intermediate Y is stored in the input dtype. MA_F32 evaluates every
+ * product as fp32 x fp32 with fp32 accumulation (fp32 matrix-core instructions
+ * at head_dim 32 to 128, the vector ALUs at 16; no reduced-precision mode).
  *
  * Errors. Every argument is checked on the host before any HIP call; a failed
  * check returns a negative ma_status and enqueues nothing. A zero-sized problem

@@ -1,8 +1,9 @@
 // attn_f32.h -- fp32 group softmax attention on the vector ALUs.
 //
-// The fp32 path of every entry point: inputs, intermediate Y and output are
-// fp32 and every product and exponential is evaluated in fp32 (no reduced-
-// precision matrix modes). One thread owns one query of a group; keys and
+// The fp32 path at head_dim 16 (head_dim 32 to 128 take the matrix-core
+// kernel of attn_f32_mfma.h): inputs, intermediate Y and output are fp32 and
+// every product and exponential is evaluated in fp32. One thread owns one
+// query of a group; keys and
 // values of the group stream through LDS in tiles and every thread reads the
 // same key row (an LDS broadcast). Online softmax (running max, rescaled sum)
 // makes one pass over the keys for groups of any length.

@@ -17,6 +17,7 @@
 #include "attn_bf16.h"
 #include "attn_bwd_bf16.h"
 #include "attn_f32.h"
+#include "attn_f32_mfma.h"
 #include "validate.h"
 
 namespace ma {
@@ -30,7 +31,7 @@ int hip_status(hipError_t e) {
   return MA_ERR_HIP;
 }
 
-enum class Kernel { kF32, kBlock, kStream };
+enum class Kernel { kF32, kF32Mfma, kBlock, kStream };
 
 // Host-side plan of one group-attention launch.
 struct Plan {
@@ -71,6 +72,16 @@ int launch_d(const Plan &pl, hipStream_t s) {
   switch (pl.kernel) {
     case Kernel::kF32:
       hipLaunchKernelGGL(group_attn_f32<D>, dim3(pl.blocks), dim3(kF32Threads), 0, s, pl.a);
+      break;
+    case Kernel::kF32Mfma:
+      if constexpr (D >= 32) {
+        if (pl.waves >= 4)
+          hipLaunchKernelGGL((group_attn_f32_mfma<D, 4>), dim3(pl.blocks), dim3(4 * 64), 0, s, pl.a);
+        else
+          hipLaunchKernelGGL((group_attn_f32_mfma<D, 2>), dim3(pl.blocks), dim3(2 * 64), 0, s, pl.a);
+      } else {
+        return MA_ERR_UNSUPPORTED;
+      }
       break;
     case Kernel::kBlock: {
       int cus = 0;
@@ -141,7 +152,13 @@ int plan_launch(const Problem &p, const GroupAddr &ga, const void *q, const void
   a.scale = (float)(1.0 / sqrt((double)p.D));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
   int q_per_block;
-  if (p.dtype == MA_F32) {
+  if (p.dtype == MA_F32 && p.D >= 32) {
+    // matrix-core fp32 kernel: waves of 32 queries, two or four per workgroup
+    const int64_t need = (qlen + kQueriesPerWave - 1) / kQueriesPerWave;
+    pl->waves = need > 2 ? 4 : 2;
+    q_per_block = kQueriesPerWave * pl->waves;
+    pl->kernel = Kernel::kF32Mfma;
+  } else if (p.dtype == MA_F32) {
     q_per_block = kF32Threads;
     pl->kernel = Kernel::kF32;
   } else if (ga.max_len <= kKeyTile && !ranged) {

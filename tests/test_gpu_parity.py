@@ -80,8 +80,8 @@ def test_small_bf16(grid, r_axes, tile, d):
     assert_bf16_parity(got, ref, "small bf16 %s r=%d tile=%s d=%d" % (grid, r_axes, tile, d))
 
 
-@pytest.mark.parametrize("d", [128, 16])
-@pytest.mark.parametrize("grid,r_axes,tile", SMALL[:4])
+@pytest.mark.parametrize("d", [128, 64, 32, 16])
+@pytest.mark.parametrize("grid,r_axes,tile", SMALL)
 def test_small_f32(grid, r_axes, tile, d):
     q, k, v = _randn(grid, 2, d, seed=200 + d)
     got, _ = run_monarch(q, k, v, grid, "f32", r_axes, tile)
@@ -109,6 +109,19 @@ def test_chunk(name):
     got_t, _ = run_monarch(q, k, v, _grid(wl), "bf16", 1, wl.tile)
     ref_t = oracle.monarch_attention(q, k, v, _grid(wl), tile=wl.tile)
     assert_bf16_parity(got_t, ref_t, name + " tiled %s" % (wl.tile,))
+
+
+def test_chunk_f32():
+    """The fp32 path (matrix-core kernel at head_dim 128) at the one-chunk workload."""
+    wl = WORKLOADS["chunk"]
+    q, k, v = make_qkv(wl)
+    got, y = run_monarch(q, k, v, _grid(wl), "f32")
+    ref, yref = oracle.monarch_attention(q, k, v, _grid(wl), return_y=True)
+    assert_f32_parity(y, yref, "chunk f32 stage R (workspace Y)")
+    assert_f32_parity(got, ref, "chunk f32 monarch")
+    got_t, _ = run_monarch(q, k, v, _grid(wl), "f32", 1, wl.tile)
+    assert_f32_parity(got_t, oracle.monarch_attention(q, k, v, _grid(wl), tile=wl.tile),
+                      "chunk f32 tiled %s" % (wl.tile,))
 
 
 @pytest.mark.timeout(900)
