@@ -44,12 +44,17 @@ struct F32Geo {
   static constexpr int DB = D / 32;                     // 32-row head_dim blocks of O^T
 };
 
+// NW = 4: two buffer sets (the next tile is stored while the current one is
+// read), two workgroups per CU. NW = 2 (groups of at most 64 members, two key
+// tiles): one buffer set and four workgroups per CU; the second tile is loaded
+// after the first has been used, while the other workgroups keep the CU busy.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void group_attn_f32_mfma(AttnLaunch p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void group_attn_f32_mfma(
+    AttnLaunch p) {
   using G = F32Geo<D>;
   constexpr int NT = NW * 64;
-  // two buffer sets: {K tile, Y^T tile}
-  __shared__ __align__(1024) unsigned char lds[2 * G::SETB];
+  constexpr int kSets = NW == 2 ? 1 : 2;
+  __shared__ __align__(1024) unsigned char lds[kSets * G::SETB];
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_f32_mfma(AttnLaunch p) 
   }
   load_tile(0);
   store_tile(0);
-  if (n > 1) load_tile(kF32MKeyTile);
+  if (kSets == 2 && n > 1) load_tile(kF32MKeyTile);
   __syncthreads();
 
   // per-lane LDS bases: key reads (row col, head_dim half*D/2 + 4c: + 16c) and
@@ -134,8 +139,8 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_f32_mfma(AttnLaunch p) 
   const float scale_log2 = p.scale_log2;
 
   for (int32_t t = 0; t < n; ++t) {
-    const unsigned char *kt = lds + (t & 1) * G::SETB + kbase;
-    const unsigned char *yt = lds + (t & 1) * G::SETB + G::KTB + ybase;
+    const unsigned char *kt = lds + (t & (kSets - 1)) * G::SETB + kbase;
+    const unsigned char *yt = lds + (t & (kSets - 1)) * G::SETB + G::KTB + ybase;
     if (wave_active) {
       // S^T = K Q^T: two accumulators (even and odd steps), summed at the end
       f32x16_t sa = {}, sb = {};
@@ -191,9 +196,15 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_f32_mfma(AttnLaunch p) 
       }
     }
     if (t + 1 < n) {
-      // buffer (t+1) % 2 was last read in step t-1, before the barrier that ended it
-      store_tile((t + 1) & 1);
-      if (t + 2 < n) load_tile((t + 2) * kF32MKeyTile);
+      if constexpr (kSets == 2) {
+        // buffer (t+1) % 2 was last read in step t-1, before the barrier that ended it
+        store_tile((t + 1) & 1);
+        if (t + 2 < n) load_tile((t + 2) * kF32MKeyTile);
+      } else {
+        __syncthreads();   // every wave is done with tile t
+        load_tile((t + 1) * kF32MKeyTile);
+        store_tile(0);
+      }
       __syncthreads();
     }
   }
