@@ -4,8 +4,8 @@
 // accumulated in fp32 (v_mfma_f32_32x32x2_f32, no reduced-precision mode),
 // and the softmax is evaluated in fp32. A workgroup of NW waves owns 32*NW
 // queries of one group and streams the group's keys and values through LDS in
-// 32-key tiles, double-buffered, with an online softmax (the same running
-// max / lazy rescale as the bf16 kernel, at fp32 weights).
+// 32-key tiles with an online softmax (the same running max / lazy rescale as
+// the bf16 kernel, at fp32 weights).
 //
 // Matrix-core formulation (C[32x32] += A[32x2] B[2x32]; lane l holds A row
 // l%32 and B column l%32 at k-slot l/32; C element r of lane l sits at row
@@ -30,8 +30,9 @@ typedef float f32x4v_t __attribute__((ext_vector_type(4)));   // a native vector
 
 // LDS tiles. K: 32 key rows of D floats; Y^T: D head_dim rows of 32 keys.
 // Each row is padded by 16 bytes, so the 16 rows one 16-byte read serves
-// (consecutive rows, same column) start 4 banks apart (of 64) and never
-// collide; every lane's reads are then one base register plus immediates.
+// (consecutive rows, same column) start on 16 distinct groups of 4 banks (of
+// 64): K rows are 132 banks apart, Y^T rows 36. Every lane's reads are then
+// one base register plus immediates.
 template <int D>
 struct F32Geo {
   static_assert(D == 32 || D == 64 || D == 128, "fp32 matrix-core path: head_dim 32, 64 or 128");
