@@ -47,7 +47,7 @@ def parse_args():
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets in the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip tiled/dense side figures")
-    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy", "backward"],
+    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy", "backward", "fp32"],
                     help="run only this kernel (or a plain device copy of one input tensor, the "
                          "calibration for byte counters; or the whole backward) --steps times on "
                          "the 21x30x52 workload; for rocprofv3")
@@ -209,11 +209,12 @@ def profile_only(which, steps, warmup=0, n_sets=3):
     wl = WORKLOADS["full"]
     T, H, W = wl.T, wl.H, wl.W
     dev = torch.device("cuda:0")
-    base = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in make_qkv(wl)]
+    dt = torch.float32 if which == "fp32" else torch.bfloat16
+    base = [torch.from_numpy(x).to(dev).to(dt) for x in make_qkv(wl)]
     sets = []
     for _ in range(n_sets):
         q, k, v = (x.clone() for x in base)
-        y = torch.empty_like(q)
+        y = torch.empty_like(q)   # also the fp32 call's workspace
         ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
         sets.append((q, k, v, y, torch.empty_like(q)))
     del base
@@ -233,6 +234,8 @@ def profile_only(which, steps, warmup=0, n_sets=3):
             ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
         elif which == "stage_r":
             ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
+        elif which == "fp32":
+            ma.monarch_attn_fwd(q, k, v, o, y, T, H, W)
         else:
             o.copy_(q)
     torch.cuda.synchronize()
