@@ -111,17 +111,19 @@ def test_chunk(name):
     assert_bf16_parity(got_t, ref_t, name + " tiled %s" % (wl.tile,))
 
 
-def test_chunk_f32():
-    """The fp32 path (matrix-core kernel at head_dim 128) at the one-chunk workload."""
-    wl = WORKLOADS["chunk"]
+@pytest.mark.parametrize("name", ["chunk", "chunk_sharp"])
+def test_chunk_f32(name):
+    """The fp32 path (matrix-core kernel at head_dim 128) at the one-chunk workload; the
+    sharp variant's peaked softmax exercises the running-max rescale."""
+    wl = WORKLOADS[name]
     q, k, v = make_qkv(wl)
     got, y = run_monarch(q, k, v, _grid(wl), "f32")
     ref, yref = oracle.monarch_attention(q, k, v, _grid(wl), return_y=True)
-    assert_f32_parity(y, yref, "chunk f32 stage R (workspace Y)")
-    assert_f32_parity(got, ref, "chunk f32 monarch")
+    assert_f32_parity(y, yref, name + " f32 stage R (workspace Y)")
+    assert_f32_parity(got, ref, name + " f32 monarch")
     got_t, _ = run_monarch(q, k, v, _grid(wl), "f32", 1, wl.tile)
     assert_f32_parity(got_t, oracle.monarch_attention(q, k, v, _grid(wl), tile=wl.tile),
-                      "chunk f32 tiled %s" % (wl.tile,))
+                      name + " f32 tiled %s" % (wl.tile,))
 
 
 @pytest.mark.timeout(900)
