@@ -37,7 +37,6 @@ __all__ = [
     "stage_r_backward",
     "stage_l_backward",
     "monarch_attention_backward",
-    "dense_attention_backward",
 ]
 
 
@@ -113,11 +112,3 @@ def monarch_attention_backward(q, k, v, do, grid: Tuple[int, int, int], r_axes: 
         return dq, dk, dv, {"dq_l": dq_l, "dk_l": dk_l, "dy": dy, "dq_r": dq_r, "dk_r": dk_r, "y": y}
     return dq, dk, dv
 
-
-def dense_attention_backward(q, k, v, do):
-    """(dq, dk, dv) of dense softmax(s Q K^T) V over all N tokens, given dO."""
-    q = np.asarray(q, np.float64)
-    N = q.shape[-2]
-    everything = [np.arange(N, dtype=np.int64)]
-    return _per_head3(lambda qq, kk, vv, gg: group_softmax_attention_backward(qq, kk, vv, gg, everything),
-                      q, k, v, do)

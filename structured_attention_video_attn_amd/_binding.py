@@ -95,12 +95,34 @@ def _check(*ts):
     for t in ts:
         if t.dim() != 4:
             raise ValueError("tensors must be [batch, heads, N, head_dim]")
-        if not t.is_cuda:
-            raise ValueError("tensors must live on the GPU")
         if t.dtype != ref.dtype or t.shape != ref.shape or t.device != ref.device:
             raise ValueError("q, k, v and out must share dtype, shape and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _check_grid(q, T, H, W):
+    """The library sees only the grid, never the tensors' size: a grid with more
+    tokens than the tensors hold would make the kernels read and write past them."""
+    if q.dim() != 4 or min(T, H, W) < 0 or q.shape[2] != T * H * W:
+        raise ValueError("q.shape[2] (%s) must equal T*H*W = %d*%d*%d"
+                         % (q.shape[2] if q.dim() == 4 else "?", T, H, W))
+
+
+def _check_workspace(ws, q):
+    """A workspace (or cache) buffer: contiguous and on q's GPU (its pointer goes to the kernels)."""
+    if ws is None:
+        return
+    if not ws.is_cuda or ws.device != q.device:
+        raise ValueError("workspace must be a GPU tensor on q's device (%s), got %s" % (q.device, ws.device))
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
 
 
 def _ptr(t):
@@ -121,18 +143,22 @@ def ma_workspace_bytes(batch, heads, T, H, W, r_axes=1, tile_t=0, tile_h=0, head
 
 
 def monarch_attn_fwd(q, k, v, out, workspace, T, H, W, r_axes=1, stream=None):
+    _check_grid(q, T, H, W)
     _check(q, k, v, out)
+    _check_workspace(workspace, q)
     B, h, N, d = q.shape
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _call("monarch_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace), ws_bytes,
           B, h, T, H, W, r_axes, d, _dtype_code(q), _stream_ptr(q, stream))
     return out
 
 
 def monarch_attn_tiled_fwd(q, k, v, out, workspace, T, H, W, tile_t, tile_h, stream=None):
+    _check_grid(q, T, H, W)
     _check(q, k, v, out)
+    _check_workspace(workspace, q)
     B, h, N, d = q.shape
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _call("monarch_attn_tiled_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
           ws_bytes, B, h, T, H, W, tile_t, tile_h, d, _dtype_code(q), _stream_ptr(q, stream))
     return out
@@ -140,9 +166,11 @@ def monarch_attn_tiled_fwd(q, k, v, out, workspace, T, H, W, tile_t, tile_h, str
 
 def monarch_attn_causal_fwd(q, k, v, out, workspace, T, H, W, chunk_t, r_axes=1, stream=None):
     """Chunk-causal Monarch over the whole sequence (bf16): chunks of chunk_t frames."""
+    _check_grid(q, T, H, W)
     _check(q, k, v, out)
+    _check_workspace(workspace, q)
     B, h, N, d = q.shape
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _call("monarch_attn_causal_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace), ws_bytes,
           B, h, T, H, W, r_axes, chunk_t, d, _dtype_code(q), _stream_ptr(q, stream))
     return out
@@ -150,6 +178,7 @@ def monarch_attn_causal_fwd(q, k, v, out, workspace, T, H, W, chunk_t, r_axes=1,
 
 def monarch_attn_chunk_fwd(q, k, v, y, out, T, H, W, t0, chunk_t, r_axes=1, stream=None):
     """One step with a cache (bf16): frames [t0, t0 + chunk_t) of y and out are written."""
+    _check_grid(q, T, H, W)
     if y is None:
         _check(q, k, v, out)
     else:
@@ -169,6 +198,7 @@ def dense_attn_fwd(q, k, v, out, stream=None):
 
 
 def ma_stage_r_fwd(q, k, v, y, T, H, W, r_axes=1, stream=None):
+    _check_grid(q, T, H, W)
     _check(q, k, v, y)
     B, h, N, d = q.shape
     _call("ma_stage_r_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(y), B, h, T, H, W, r_axes, d,
@@ -177,6 +207,7 @@ def ma_stage_r_fwd(q, k, v, y, T, H, W, r_axes=1, stream=None):
 
 
 def ma_stage_l_fwd(q, k, y, out, T, H, W, r_axes=1, tile_t=0, tile_h=0, stream=None):
+    _check_grid(q, T, H, W)
     _check(q, k, y, out)
     B, h, N, d = q.shape
     _call("ma_stage_l_fwd", _ptr(q), _ptr(k), _ptr(y), _ptr(out), B, h, T, H, W, r_axes, tile_t,
@@ -194,11 +225,13 @@ def monarch_attn_bwd(q, k, v, out, dout, dq, dk, dv, workspace, T, H, W, r_axes=
                      tile_h=0, stream=None, y=None):
     """dq, dk, dv of the forward (same r_axes / tile) given dout; bf16 only. `y`: the
     forward's Y (its workspace viewed as q's shape) to skip recomputing stage R, or None."""
+    _check_grid(q, T, H, W)
     _check(q, k, v, out, dout, dq, dk, dv)
     if y is not None:
         _check(q, y)
+    _check_workspace(workspace, q)
     B, h, N, d = q.shape
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _call("monarch_attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(y), _ptr(dq),
           _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, h, T, H, W, r_axes, tile_t, tile_h, d,
           _dtype_code(q), _stream_ptr(q, stream))

@@ -252,3 +252,32 @@ def test_causal_and_chunk_argument_errors(lib):
     assert s(q, k, v, y, q, *good, 1, 18, 3, 128, BF16, None) == INVALID     # out aliases q
     assert s(q, k, v, y, o, 1, 12, 21, 30, 52, 1, 18, 3, 48, BF16, None) == UNSUPPORTED
     assert s(None, None, None, None, None, 0, 12, 21, 30, 52, 1, 18, 3, 128, BF16, None) == OK
+
+
+def test_binding_rejects_grid_that_does_not_match_tensors():
+    # The C ABI never sees the tensors' token count: the binding must refuse a grid
+    # whose T*H*W differs from q.shape[2] before any pointer reaches the library.
+    import torch
+    import structured_attention_video_attn_amd as ma
+    q = torch.empty(1, 2, 30, 16)
+    calls = [
+        lambda: ma.monarch_attn_fwd(q, q, q, q, None, 2, 4, 4),
+        lambda: ma.monarch_attn_tiled_fwd(q, q, q, q, None, 2, 4, 4, 1, 2),
+        lambda: ma.monarch_attn_causal_fwd(q, q, q, q, None, 2, 4, 4, 1),
+        lambda: ma.monarch_attn_chunk_fwd(q, q, q, q, q, 2, 4, 4, 0, 1),
+        lambda: ma.ma_stage_r_fwd(q, q, q, q, 2, 4, 4),
+        lambda: ma.ma_stage_l_fwd(q, q, q, q, 2, 4, 4),
+        lambda: ma.monarch_attn_bwd(q, q, q, q, q, q, q, q, None, 2, 4, 4),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match=r"T\*H\*W"):
+            call()
+
+
+def test_binding_rejects_host_workspace():
+    import torch
+    from structured_attention_video_attn_amd import _binding
+    q = torch.empty(1, 1, 32, 16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _binding._check_workspace(torch.empty(512), q)
+    _binding._check_workspace(None, q)   # no workspace: nothing to check

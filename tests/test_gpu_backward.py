@@ -138,12 +138,32 @@ def test_backward_structured_tiled_two_heads():
           "structured bwd tiled %s (2 heads)" % (wl.tile,))
 
 
-@pytest.mark.timeout(600)
-def test_backward_full_scale_dv_sum():
-    # summed over all tokens, dV equals the summed dO (both factors are row-stochastic)
+@pytest.mark.timeout(900)
+def test_backward_full_scale_all_heads_and_dv_sum():
+    """All 12 heads at 21x30x52 compared whole with the backward oracle, and the
+    oracle-free identity: summed over tokens, dV equals the summed dO (both factors
+    are row-stochastic).
+
+    Tolerance of the identity, from the bf16 roundings on the path (each a
+    round-to-nearest with relative error uniform in +-2^-9, standard deviation
+    2^-9/sqrt(3) of the rounded value, independent across elements): dv stored in
+    bf16 (sum of dv^2), dY stored in bf16 and the stage-R weights rounded to bf16 as
+    MFMA operands (each weighted by dY; per-row weight sums deviate by at most that
+    relative amount, sum of P^2 <= 1), the stage-L weights rounded the same way
+    (weighted by dO). The column sum's error then has standard deviation at most
+    2^-9/sqrt(3) * sqrt(sum dv^2 + 2 sum dY^2 + sum dO^2); the gate is six of them."""
     wl = WORKLOADS["full"]
     q, k, v = make_qkv(wl)
     do = to_bf16_f32(np.random.default_rng(33).standard_normal(q.shape, dtype=np.float32))
-    _, _, dv = run_bwd(q, k, v, do, (wl.T, wl.H, wl.W))
-    lhs, rhs = dv.sum(axis=2), do.sum(axis=2)
-    assert np.abs(lhs - rhs).max() <= 1e-2 * np.abs(rhs).max() + 0.5
+    grid = (wl.T, wl.H, wl.W)
+    got = run_bwd(q, k, v, do, grid)
+    dq, dk, dv_ref, parts = mb.monarch_attention_backward(q, k, v, do, grid, return_parts=True)
+    check(got, (dq, dk, dv_ref), "full bwd (12 heads)")
+    dv = got[2]
+    do64 = do.astype(np.float64)
+    lhs, rhs = dv.sum(axis=2), do64.sum(axis=2)
+    sigma = 2.0 ** -9 / np.sqrt(3.0) * np.sqrt((dv ** 2).sum(axis=2) + 2.0 * (parts["dy"] ** 2).sum(axis=2)
+                                                + (do64 ** 2).sum(axis=2))
+    worst = float((np.abs(lhs - rhs) / sigma).max())
+    print("sum dV - sum dO: max |err| = %.3e, max |err| / sigma = %.2f" % (np.abs(lhs - rhs).max(), worst))
+    assert worst <= 6.0

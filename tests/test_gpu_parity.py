@@ -1,7 +1,8 @@
 """GPU parity: the HIP library through its C ABI against the fp64 CPU oracle.
 
 Sizes: the oracle covers the small cases and the 4680- and 32760-token
-workloads whole; at 126360 tokens it checks seeded samples of output rows.
+workloads whole; at 126360 tokens it covers four seeded heads whole and
+seeded rows of every head.
 bf16 cases pass the max-abs 2e-2 gate plus the relative gates G1/G2 of
 parity_util; fp32 cases pass max-abs 1e-5.
 """
@@ -149,19 +150,23 @@ def test_structured_tiled():
 
 
 @pytest.mark.timeout(900)
-def test_long_sampled():
+def test_long_whole_heads():
+    """126360 tokens, 16 heads: four seeded heads compared whole (every output row),
+    untiled (stage-L groups of 2430 over 38 key tiles) and in 9 x 30 tiles (boxes of 270),
+    plus seeded rows of every head through the row-wise oracle."""
     wl = WORKLOADS["long"]
     q, k, v = make_qkv(wl)
     rng = np.random.default_rng(44)
     heads = sorted(rng.choice(wl.heads, size=4, replace=False).tolist())
-    rows = sorted(rng.choice(wl.n_tokens, size=48, replace=False).tolist()) + [0, wl.n_tokens - 1]
+    rows = sorted(rng.choice(wl.n_tokens, size=4, replace=False).tolist()) + [0, wl.n_tokens - 1]
+    qh, kh, vh = (np.ascontiguousarray(x[:, heads]) for x in (q, k, v))
     for tile in (None, wl.tile):
         got, _ = run_monarch(q, k, v, _grid(wl), "bf16", 1, tile)
         assert np.isfinite(got).all()
-        sub = got[:, heads][:, :, rows]
-        ref = oracle.monarch_attention_rows(q[:, heads], k[:, heads], v[:, heads], _grid(wl), rows,
-                                            tile=tile)
-        assert_bf16_parity(sub, ref, "long tile=%s (4 heads x %d rows)" % (tile, len(rows)))
+        ref = oracle.monarch_attention(qh, kh, vh, _grid(wl), tile=tile)
+        assert_bf16_parity(got[:, heads], ref, "long tile=%s (heads %s whole)" % (tile, heads))
+        ref_rows = oracle.monarch_attention_rows(q, k, v, _grid(wl), rows, tile=tile)
+        assert_bf16_parity(got[:, :, rows], ref_rows, "long tile=%s (16 heads x %d rows)" % (tile, len(rows)))
 
 
 @pytest.mark.timeout(600)
@@ -190,16 +195,18 @@ def test_frame_blocks_chunk():
 
 
 @pytest.mark.timeout(600)
-def test_frame_blocks_full_sampled():
+def test_frame_blocks_full_whole_heads():
+    """r_axes = 2 at 32760 tokens: three seeded heads compared whole (stage R over 21
+    frames of 1560 tokens, 25 key tiles each; stage L over groups of 21)."""
     wl = WORKLOADS["full"]
     q, k, v = make_qkv(wl)
     got, _ = run_monarch(q, k, v, _grid(wl), "bf16", 2)
     assert np.isfinite(got).all()
     rng = np.random.default_rng(46)
     heads = sorted(rng.choice(wl.heads, size=3, replace=False).tolist())
-    rows = sorted(rng.choice(wl.n_tokens, size=40, replace=False).tolist()) + [0, wl.n_tokens - 1]
-    ref = oracle.monarch_attention_rows(q[:, heads], k[:, heads], v[:, heads], _grid(wl), rows, r_axes=2)
-    assert_bf16_parity(got[:, heads][:, :, rows], ref, "full r_axes=2 (3 heads x %d rows)" % len(rows))
+    qh, kh, vh = (np.ascontiguousarray(x[:, heads]) for x in (q, k, v))
+    ref = oracle.monarch_attention(qh, kh, vh, _grid(wl), r_axes=2)
+    assert_bf16_parity(got[:, heads], ref, "full r_axes=2 (heads %s whole)" % (heads,))
 
 
 # ------------------------------------------------------------------ closed forms at full scale
