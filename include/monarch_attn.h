@@ -50,7 +50,8 @@ typedef enum {
   MA_ERR_UNSUPPORTED = -2,  /* head_dim not in {16,32,64,128}, dtype unknown, size limits */
   MA_ERR_ALIGNMENT = -3,    /* a pointer is not 16-byte aligned */
   MA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than ma_workspace_bytes() */
-  MA_ERR_HIP = -5           /* the HIP runtime rejected a launch */
+  MA_ERR_HIP = -5,          /* the HIP runtime rejected a launch */
+  MA_ERR_SCRATCH = -6       /* monarch_attn_fwd_noalloc: Y larger than the fixed buffer */
 } ma_status;
 
 typedef enum { MA_BF16 = 0, MA_F32 = 1 } ma_dtype;
@@ -78,6 +79,25 @@ int monarch_attn_fwd(const void *q, const void *k, const void *v, void *out,
                      int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
                      int32_t r_axes, int32_t head_dim, int32_t dtype,
                      struct ihipStream_t *stream);
+
+/* monarch_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same operation, arguments, checks and
+ * kernels as monarch_attn_fwd; the stage-R output Y goes to a buffer the
+ * library holds per GPU (ma_noalloc_scratch_bytes() = 128 MiB, reserved on
+ * each GPU the library is loaded on until the process ends). The call
+ * allocates nothing. MA_ERR_SCRATCH when Y (ma_workspace_bytes(...) bytes)
+ * is larger than that buffer. Every call on one GPU uses the same buffer:
+ * calls on one GPU must not overlap in time (issue them on one stream, or
+ * order streams with events); overlapping calls race on it. The buffer keeps
+ * the last call's Y; nothing in it needs to start at any value. */
+int monarch_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out,
+                             int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+                             int32_t r_axes, int32_t head_dim, int32_t dtype,
+                             struct ihipStream_t *stream);
+
+/* Size in bytes of the per-GPU buffer behind monarch_attn_fwd_noalloc. */
+size_t ma_noalloc_scratch_bytes(void);
 
 /* Tiled Monarch attention: as monarch_attn_fwd with r_axes = 1, but each
  * stage-L softmax runs only over the box {(t', h') : t'/tile_t = t/tile_t,

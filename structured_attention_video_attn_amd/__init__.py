@@ -18,5 +18,7 @@ from ._binding import (  # noqa: F401
     monarch_attn_causal_fwd,
     monarch_attn_chunk_fwd,
     monarch_attn_fwd,
+    monarch_attn_fwd_noalloc,
+    ma_noalloc_scratch_bytes,
     monarch_attn_tiled_fwd,
 )

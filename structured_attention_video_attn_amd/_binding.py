@@ -31,6 +31,8 @@ _SIZE = ctypes.c_size_t
 SIGNATURES = {
     "ma_workspace_bytes": (_SIZE, [_I32] * 10),
     "monarch_attn_fwd": (ctypes.c_int, [_PTR] * 5 + [_SIZE] + [_I32] * 8 + [_PTR]),
+    "monarch_attn_fwd_noalloc": (ctypes.c_int, [_PTR] * 4 + [_I32] * 8 + [_PTR]),
+    "ma_noalloc_scratch_bytes": (_SIZE, []),
     "monarch_attn_tiled_fwd": (ctypes.c_int, [_PTR] * 5 + [_SIZE] + [_I32] * 9 + [_PTR]),
     "monarch_attn_causal_fwd": (ctypes.c_int, [_PTR] * 5 + [_SIZE] + [_I32] * 9 + [_PTR]),
     "monarch_attn_chunk_fwd": (ctypes.c_int, [_PTR] * 5 + [_I32] * 10 + [_PTR]),
@@ -151,6 +153,20 @@ def monarch_attn_fwd(q, k, v, out, workspace, T, H, W, r_axes=1, stream=None):
     _call("monarch_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace), ws_bytes,
           B, h, T, H, W, r_axes, d, _dtype_code(q), _stream_ptr(q, stream))
     return out
+
+
+def monarch_attn_fwd_noalloc(q, k, v, out, T, H, W, r_axes=1, stream=None):
+    """monarch_attn_fwd with Y in the library's fixed per-GPU buffer: no workspace, no allocation."""
+    _check_grid(q, T, H, W)
+    _check(q, k, v, out)
+    B, h, N, d = q.shape
+    _call("monarch_attn_fwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h, T, H, W, r_axes, d,
+          _dtype_code(q), _stream_ptr(q, stream))
+    return out
+
+
+def ma_noalloc_scratch_bytes() -> int:
+    return int(load_library().ma_noalloc_scratch_bytes())
 
 
 def monarch_attn_tiled_fwd(q, k, v, out, workspace, T, H, W, tile_t, tile_h, stream=None):

@@ -12,6 +12,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/monarch_attn.h"
 #include "attn_bf16.h"
@@ -29,6 +30,37 @@ int hip_status(hipError_t e) {
   if (e == hipSuccess) return MA_OK;
   g_last_hip_error = (int)e;
   return MA_ERR_HIP;
+}
+
+// ------------------------------------------------- fixed buffer of the no-allocation entry point
+// monarch_attn_fwd_noalloc keeps the stage-R output Y in this array instead of a
+// caller's workspace. Each GPU the library runs on holds its own copy (allocated
+// when the code object is loaded, kept until the process ends). In host code the
+// name is only a stand-in: the device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device (looked up once per device).
+int scratch_address(void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < kMaxDevices && addr[dev] != nullptr) {
+    *out = addr[dev];
+    return MA_OK;
+  }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_status(e);
+  if (p == nullptr) return MA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) addr[dev] = p;
+  *out = p;
+  return MA_OK;
 }
 
 enum class Kernel { kF32, kF32Mfma, kBlock, kStream };
@@ -422,6 +454,28 @@ int monarch_attn_fwd(const void *q, const void *k, const void *v, void *out, voi
                         0, false, head_dim, dtype, stream);
 }
 
+int monarch_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int32_t batch,
+                             int32_t heads, int32_t T, int32_t H, int32_t W, int32_t r_axes, int32_t head_dim,
+                             int32_t dtype, struct ihipStream_t *stream) {
+  // every host-side check first, as in monarch_attn_fwd, then the buffer's address
+  Problem p;
+  int st = resolve_grid(batch, heads, T, H, W, r_axes, 0, 0, false, head_dim, dtype, &p);
+  if (st != MA_OK || p.empty) return st;
+  st = check_tensor_ptrs(q, k, v, out, p.tensor_bytes);
+  if (st != MA_OK) return st;
+  const size_t need = workspace_needed(p);
+  if (need > kScratchBytes) return MA_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != MA_OK) return st;
+  }
+  return monarch_common(q, k, v, out, ws, need > 0 ? kScratchBytes : 0, batch, heads, T, H, W, r_axes, 0, 0,
+                        false, head_dim, dtype, stream);
+}
+
+size_t ma_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 int monarch_attn_tiled_fwd(const void *q, const void *k, const void *v, void *out, void *workspace,
                            size_t workspace_bytes, int32_t batch, int32_t heads, int32_t T,
                            int32_t H, int32_t W, int32_t tile_t, int32_t tile_h, int32_t head_dim,
@@ -627,6 +681,7 @@ const char *ma_status_string(int status) {
     case MA_ERR_ALIGNMENT: return "MA_ERR_ALIGNMENT: a pointer is not 16-byte aligned";
     case MA_ERR_WORKSPACE: return "MA_ERR_WORKSPACE: workspace missing or too small";
     case MA_ERR_HIP: return "MA_ERR_HIP: the HIP runtime rejected a launch";
+    case MA_ERR_SCRATCH: return "MA_ERR_SCRATCH: the problem needs more than the library's fixed buffer (ma_noalloc_scratch_bytes)";
     default: return "unknown ma_status";
   }
 }

@@ -116,6 +116,30 @@ def test_monarch_argument_errors(lib):
     assert call(q=None, k=None, v=None, o=None, w=None, W=0) == OK
 
 
+def test_noalloc_argument_errors(lib):
+    # Every check of the no-allocation entry point runs before any HIP call,
+    # including the size limit of its fixed per-GPU buffer.
+    SCRATCH = -6
+    f = lib.monarch_attn_fwd_noalloc
+    cap = lib.ma_noalloc_scratch_bytes()
+    assert cap == 128 << 20
+    q, k, v, o = _ptrs(4)
+
+    def call(q=q, k=k, v=v, o=o, batch=1, heads=12, T=21, H=30, W=52, r=1, d=128, dt=BF16):
+        return f(q, k, v, o, batch, heads, T, H, W, r, d, dt, None)
+
+    assert lib.ma_workspace_bytes(1, 24, 21, 30, 52, 1, 0, 0, 128, BF16) > cap
+    assert call(heads=24) == SCRATCH               # Y of 201 MB does not fit
+    assert call(heads=12, dt=F32) == SCRATCH       # fp32: Y of 201 MB
+    assert call(q=None) == INVALID
+    assert call(o=q) == INVALID
+    assert call(v=A16 + 2 * BIG + 8) == ALIGN
+    assert call(r=5) == INVALID
+    assert call(d=24) == UNSUPPORTED
+    assert call(q=None, k=None, v=None, o=None, heads=0) == OK
+    assert lib.ma_status_string(SCRATCH).startswith(b"MA_ERR_SCRATCH")
+
+
 def test_tiled_and_stage_argument_errors(lib):
     q, k, v, o, w = _ptrs()
     nb = 1 << 28
