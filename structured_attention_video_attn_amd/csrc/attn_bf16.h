@@ -367,6 +367,17 @@ __device__ __forceinline__ void exp_pair(const f32x16_t &s, int r, float scale_l
   pb[r / 8][r % 8 + 1] = pr[1];
 }
 
+// The same for scores that already are log2-scaled and relative to the running
+// reference (the streaming kernel folds both into the QK accumulator).
+__device__ __forceinline__ void exp_pair_shifted(const f32x16_t &s, int r, float &lsum, bf16x8_t (&pb)[2]) {
+  const float e0 = __builtin_amdgcn_exp2f(s[r]);
+  const float e1 = __builtin_amdgcn_exp2f(s[r + 1]);
+  const bf16x2_t pr = __builtin_convertvector((f32x2_t){e0, e1}, bf16x2_t);   // v_cvt_pk_bf16_f32
+  lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, (bf16x2_t){(__bf16)1.f, (__bf16)1.f}, lsum, false);
+  pb[r / 8][r % 8] = pr[0];
+  pb[r / 8][r % 8 + 1] = pr[1];
+}
+
 // Per-lane LDS byte offsets of the streaming tile's fragment reads, relative
 // to the tile buffer: computed once per kernel, so that each read is one
 // ds_read with the buffer (and row-block) base in its immediate offset. The
@@ -414,9 +425,10 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int col, int half, int tr
 // weights free of any write to the accumulators that block 0's MFMAs update.
 template <int D, typename FQ, typename FP>
 __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsigned char *vs,
-                                            const bf16x8_t *qb, int32_t k0, int32_t len, float scale_log2,
-                                            float &m_run, float &l_run, f32x16_t *oacc, int half, int tr_col,
-                                            const LaneOffsets<D> &lo, FQ &&on_qk, FP &&on_pv) {
+                                            const bf16x8_t *qb, int32_t k0, int32_t len, bool first,
+                                            f32x16_t &negm, float &m_run, float &l_run, f32x16_t *oacc,
+                                            int half, int tr_col, const LaneOffsets<D> &lo, FQ &&on_qk,
+                                            FP &&on_pv) {
   using G = TileGeo<D>;
   constexpr int DK = G::DK, DB = G::DB;
   constexpr int AK = DK < 2 ? DK : 2;   // k-steps of key fragments in flight
@@ -428,7 +440,9 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
   };
 #pragma unroll
   for (int j = 0; j < AK; ++j) read_k(j);
-  f32x16_t s0 = {}, s1 = {};
+  // the accumulators start at -m_run: the MFMAs deliver s*log2(e)*q.k - m_run
+  // (the queries were scaled by s*log2(e) when loaded)
+  f32x16_t s0 = negm, s1 = negm;
 #pragma unroll
   for (int j = 0; j < DK; ++j) {
     __builtin_amdgcn_sched_barrier(0);
@@ -448,25 +462,40 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
       if (key + 32 >= len) s1[r] = -INFINITY;
     }
   }
-  float mx = fmaxf(s0[0], s1[0]);
+  // tile max of the shifted scores: two chains of three-input maxima
+  float mx0 = fmaxf(fmaxf(s0[0], s0[1]), s0[2]), mx1 = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  for (int r = 3; r < 15; r += 2) {
+    mx0 = fmaxf(fmaxf(mx0, s0[r]), s0[r + 1]);
+    mx1 = fmaxf(fmaxf(mx1, s1[r]), s1[r + 1]);
+  }
+  float mx = fmaxf(fmaxf(mx0, s0[15]), fmaxf(mx1, s1[15]));
   mx = fmaxf(mx, swap_halves(mx));   // the other 16 keys of each block for this query
-  const float tmax = mx * scale_log2;
-  if (__any(tmax > m_run + kLazyRescale)) {
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
+  // The reference m_run only moves when a score exceeds it by more than
+  // kLazyRescale, and at the first tile (which sets it from that tile's max).
+  if (__any(first || mx > kLazyRescale)) {
+    const float delta = first ? mx : fmaxf(mx, 0.f);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      l_run *= alpha;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-    m_run = m_new;
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] -= delta;
+      s1[r] -= delta;
+    }
+    m_run += delta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_run;
   }
   float lsum = 0.f;
   bf16x8_t p0[2], p1[2];
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) exp_pair(s0, r, scale_log2, m_run, lsum, p0);
+  for (int r = 0; r < 16; r += 2) exp_pair_shifted(s0, r, lsum, p0);
 
   // ---- O^T += Y^T P^T: step i covers block kb = i / 2DB, keys +16h (h = i / DB % 2), d-block b = i % DB
   constexpr int NPV = 4 * DB;
@@ -492,7 +521,7 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
     if (i + AV < NPV) read_y(i + AV);
     if (i < 2 * DB) {
 #pragma unroll
-      for (int e = 0; e < EPS; e += 2) exp_pair(s1, EPS * i + e, scale_log2, m_run, lsum, p1);
+      for (int e = 0; e < EPS; e += 2) exp_pair_shifted(s1, EPS * i + e, lsum, p1);
     }
     on_pv(i);
   }
@@ -506,21 +535,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// One work item of the streaming kernel: logical workgroup `bid` (query tile,
+// span, group and (batch, head) slice decoded from it). `lds` is the caller's
+// LDS array of five tile buffers, value ring first: inlined into a kernel
+// whose __shared__ array it is, each buffer sits at a constant offset, which
+// the fragment reads carry in their immediate offsets. Ends with every DMA
+// landed; the caller separates consecutive items by a barrier.
 template <int D, int NW, bool kTwoLevel>
-__global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
+__device__ __forceinline__ void stream_item(const AttnLaunch &p, uint32_t bid, unsigned char *lds) {
   using G = TileGeo<D>;
   static_assert(G::NINST % NW == 0, "every wave must issue the same number of DMA instructions");
   constexpr int WPT = G::NINST / NW;         // DMA windows per tile, tensor and wave
-  // One LDS array with the five tile buffers at fixed offsets (value ring
-  // first): the unrolled steps below address each buffer by a constant, which
-  // the fragment reads carry in their immediate offsets.
-  __shared__ __align__(1024) unsigned char lds[5 * G::TILEB];
   unsigned char *const yt0 = lds, *const yt1 = lds + G::TILEB;
   unsigned char *const kt0 = lds + 2 * G::TILEB, *const kt1 = lds + 3 * G::TILEB, *const kt2 = lds + 4 * G::TILEB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const bool packed = p.span_waves > 0;
   const int32_t qt = (int32_t)(bid % (uint32_t)p.n_qtiles);
   const uint32_t rest0 = bid / (uint32_t)p.n_qtiles;
@@ -650,13 +680,27 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
   {
     const unsigned char *qtile = (wave < 2 ? yt1 : kt2) + (wave & 1) * 32 * G::ROWB;
 #pragma unroll
-    for (int j = 0; j < G::DK; ++j) qb[j] = *reinterpret_cast<const bf16x8_t *>(qtile + lo.k[j]);
+    for (int j = 0; j < G::DK; ++j) {
+      // scaled by s*log2(e) and rounded back to bf16, so that the QK MFMAs
+      // deliver softmax exponents in log2 units
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(qtile + lo.k[j]);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pr = __builtin_convertvector(
+            (f32x2_t){(float)x[e] * p.scale_log2, (float)x[e + 1] * p.scale_log2}, bf16x2_t);
+        qb[j][e] = pr[0];
+        qb[j][e + 1] = pr[1];
+      }
+    }
   }
 
   f32x16_t oacc[G::DB];
 #pragma unroll
   for (int b = 0; b < G::DB; ++b) oacc[b] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_run: the reference subtracted from every log2-scaled score (set from the
+  // first tile's max); negm holds -m_run as the QK accumulators' initial value
+  float m_run = 0.f, l_run = 0.f;
+  f32x16_t negm = {};
 
   constexpr int NQ = G::DK;        // QK hook points per tile
   constexpr int NP = 4 * G::DB;    // PV hook points per tile
@@ -685,7 +729,7 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
       auto on_pv = [&](int i) __attribute__((always_inline)) {
         if (kDma && i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
-      stream_tile<D>(kc, yc, qb, t * kKeyTile, qhi, p.scale_log2, m_run, l_run, oacc, half, tr_col, lo,
+      stream_tile<D>(kc, yc, qb, t * kKeyTile, qhi, t == 0, negm, m_run, l_run, oacc, half, tr_col, lo,
                      on_qk, on_pv);
       if constexpr (kDma) {
 #pragma unroll
@@ -752,6 +796,12 @@ __global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
     const int32_t m = q0 + r;
     if (m < qhi) *reinterpret_cast<uint4 *>(oh + (uint32_t)member_token(geo, m) * D + 8 * c) = v;
   }
+}
+
+template <int D, int NW, bool kTwoLevel>
+__global__ __launch_bounds__(NW * 64, 2) void group_attn_bf16(AttnLaunch p) {
+  __shared__ __align__(1024) unsigned char lds[5 * TileGeo<D>::TILEB];
+  stream_item<D, NW, kTwoLevel>(p, xcd_remap(blockIdx.x, gridDim.x), lds);
 }
 
 // ---------------------------------------------------------------------------
