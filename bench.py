@@ -336,7 +336,7 @@ def main():
     torch.cuda.synchronize()
     for i in range(args.steps):
         q, k, v, o, ws = sets[i % len(sets)]
-        y = ws.view(q.shape)
+        y = ws[:q.numel()].view(q.shape)
         ev[i][0].record(stream)
         ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
         ev[i][1].record(stream)
@@ -403,7 +403,7 @@ def main():
 
         def chunk_step(i):
             q_, k_, v_, o_, ws_ = sets[i % len(sets)]
-            ma.monarch_attn_chunk_fwd(q_, k_, v_, ws_.view(q_.shape), o_, T, H, W, t0, ct)
+            ma.monarch_attn_chunk_fwd(q_, k_, v_, ws_[:q_.numel()].view(q_.shape), o_, T, H, W, t0, ct)
         ms_step = time_loop(chunk_step, args.steps, args.warmup)
         fsz = H * W
         nq = ct * fsz                     # tokens of the chunk

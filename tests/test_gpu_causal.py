@@ -159,4 +159,4 @@ def test_first_chunk_equals_monarch_of_its_frames():
     ma.monarch_attn_fwd(*sub, o2, ws, ct, H, W)
     torch.cuda.synchronize()
     assert torch.equal(out[:, :, :n], o2)
-    assert torch.equal(y[:, :, :n], ws.view(o2.shape))
+    assert torch.equal(y[:, :, :n], ws[:o2.numel()].view(o2.shape))
