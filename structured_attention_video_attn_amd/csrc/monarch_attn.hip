@@ -103,7 +103,13 @@ template <int D>
 int launch_d(const Plan &pl, hipStream_t s) {
   switch (pl.kernel) {
     case Kernel::kF32:
-      hipLaunchKernelGGL(group_attn_f32<D>, dim3(pl.blocks), dim3(kF32Threads), 0, s, pl.a);
+      // the vector-ALU fp32 kernel serves head_dim 16 only (plan_launch sends
+      // 32..128 to the matrix-core kernel), so it is instantiated for 16 only
+      if constexpr (D == 16) {
+        hipLaunchKernelGGL(group_attn_f32<D>, dim3(pl.blocks), dim3(kF32Threads), 0, s, pl.a);
+      } else {
+        return MA_ERR_UNSUPPORTED;
+      }
       break;
     case Kernel::kF32Mfma:
       if constexpr (D >= 32) {
