@@ -47,10 +47,11 @@ def parse_args():
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets in the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip tiled/dense side figures")
-    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy", "backward", "fp32"],
+    ap.add_argument("--profile-only", choices=["stage_l", "stage_r", "copy", "backward", "fp32", "stage_l_tiled"],
                     help="run only this kernel (or a plain device copy of one input tensor, the "
                          "calibration for byte counters; or the whole backward) --steps times on "
-                         "the 21x30x52 workload; for rocprofv3")
+                         "the 21x30x52 workload (stage_l_tiled: stage L in 3x30 tiles on the "
+                         "structured workload); for rocprofv3")
     ap.add_argument("--profile-warmup", type=int, default=0,
                     help="with --profile-only: launches before the --steps profiled ones (clock ramp)")
     ap.add_argument("--summarize-counters", nargs=4,
@@ -58,7 +59,7 @@ def parse_args():
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv output (kernel runs and "
                          "copy runs) into the per-launch HBM traffic of --kernel, written to "
                          "profiles/traffic_full_<kernel>.json")
-    ap.add_argument("--kernel", default="stage_l", choices=["stage_l", "stage_r"])
+    ap.add_argument("--kernel", default="stage_l", choices=["stage_l", "stage_r", "stage_l_tiled"])
     return ap.parse_args()
 
 
@@ -159,7 +160,7 @@ def cpu_baseline(wl, q, k, v):
                       "(stage R + stage L), %.1f s wall" % (calls, el)}
 
 
-KERNEL_SYMBOL = {"stage_l": "group_attn_bf16", "stage_r": "block_attn_bf16"}
+KERNEL_SYMBOL = {"stage_l": "group_attn_bf16", "stage_r": "block_attn_bf16", "stage_l_tiled": "group_attn_bf16"}
 
 
 def _counter_rows(d, counter):
@@ -241,7 +242,7 @@ def profile_only(which, steps, warmup=0, n_sets=3):
     import structured_attention_video_attn_amd as ma
     from workloads import WORKLOADS, make_qkv
     ma.load_library()
-    wl = WORKLOADS["full"]
+    wl = WORKLOADS["structured" if which == "stage_l_tiled" else "full"]
     T, H, W = wl.T, wl.H, wl.W
     dev = torch.device("cuda:0")
     dt = torch.float32 if which == "fp32" else torch.bfloat16
@@ -267,6 +268,8 @@ def profile_only(which, steps, warmup=0, n_sets=3):
             ma.monarch_attn_bwd(q, k, v, o, dout, *grads, wsb, T, H, W)
         elif which == "stage_l":
             ma.ma_stage_l_fwd(q, k, y, o, T, H, W)
+        elif which == "stage_l_tiled":
+            ma.ma_stage_l_fwd(q, k, y, o, T, H, W, 1, wl.tile[0], wl.tile[1])
         elif which == "stage_r":
             ma.ma_stage_r_fwd(q, k, v, y, T, H, W)
         elif which == "fp32":
