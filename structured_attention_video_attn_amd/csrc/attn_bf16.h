@@ -423,7 +423,10 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int col, int half, int tr
 //                            weights of block 1, two scores per slot (DB = 4)
 // One rescale decision per tile (instead of per 32-key block) keeps block 1's
 // weights free of any write to the accumulators that block 0's MFMAs update.
-template <int D, typename FQ, typename FP>
+// kHalf: the tile's second 32-key block lies wholly past the keys (a group's
+// ragged last tile), so only block 0's products and weights are formed, in the
+// same order as in a full tile (the results are the full tile's, bit for bit).
+template <int D, bool kHalf = false, typename FQ, typename FP>
 __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsigned char *vs,
                                             const bf16x8_t *qb, int32_t k0, int32_t len, bool first,
                                             f32x16_t &negm, float &m_run, float &l_run, f32x16_t *oacc,
@@ -436,18 +439,19 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
   auto read_k = [&](int j) __attribute__((always_inline)) {
     // rows col and 32 + col share the swizzle (it depends on the row mod 16)
     kf0[j] = *reinterpret_cast<const bf16x8_t *>(ks + lo.k[j]);
-    kf1[j] = *reinterpret_cast<const bf16x8_t *>(ks + 32 * G::ROWB + lo.k[j]);
+    if constexpr (!kHalf) kf1[j] = *reinterpret_cast<const bf16x8_t *>(ks + 32 * G::ROWB + lo.k[j]);
   };
 #pragma unroll
   for (int j = 0; j < AK; ++j) read_k(j);
   // the accumulators start at -m_run: the MFMAs deliver s*log2(e)*q.k - m_run
   // (the queries were scaled by s*log2(e) when loaded)
-  f32x16_t s0 = negm, s1 = negm;
+  f32x16_t s0 = negm, s1;
+  if constexpr (!kHalf) s1 = negm;
 #pragma unroll
   for (int j = 0; j < DK; ++j) {
     __builtin_amdgcn_sched_barrier(0);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0[j], qb[j], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[j], qb[j], s1, 0, 0, 0);
+    if constexpr (!kHalf) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1[j], qb[j], s1, 0, 0, 0);
     if (j + AK < DK) read_k(j + AK);
     on_qk(j);
   }
@@ -459,17 +463,28 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
     for (int r = 0; r < 16; ++r) {
       const int32_t key = k0 + 8 * (r / 4) + 4 * half + (r % 4);
       if (key >= len) s0[r] = -INFINITY;
-      if (key + 32 >= len) s1[r] = -INFINITY;
+      if (!kHalf && key + 32 >= len) s1[r] = -INFINITY;
     }
   }
   // tile max of the shifted scores: two chains of three-input maxima
-  float mx0 = fmaxf(fmaxf(s0[0], s0[1]), s0[2]), mx1 = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
+  float mx;
+  if constexpr (kHalf) {
+    float m0 = fmaxf(fmaxf(s0[0], s0[1]), s0[2]), m1 = fmaxf(fmaxf(s0[3], s0[4]), s0[5]);
 #pragma unroll
-  for (int r = 3; r < 15; r += 2) {
-    mx0 = fmaxf(fmaxf(mx0, s0[r]), s0[r + 1]);
-    mx1 = fmaxf(fmaxf(mx1, s1[r]), s1[r + 1]);
+    for (int r = 6; r < 14; r += 4) {
+      m0 = fmaxf(fmaxf(m0, s0[r]), s0[r + 1]);
+      m1 = fmaxf(fmaxf(m1, s0[r + 2]), s0[r + 3]);
+    }
+    mx = fmaxf(fmaxf(m0, s0[14]), fmaxf(m1, s0[15]));
+  } else {
+    float mx0 = fmaxf(fmaxf(s0[0], s0[1]), s0[2]), mx1 = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+      mx0 = fmaxf(fmaxf(mx0, s0[r]), s0[r + 1]);
+      mx1 = fmaxf(fmaxf(mx1, s1[r]), s1[r + 1]);
+    }
+    mx = fmaxf(fmaxf(mx0, s0[15]), fmaxf(mx1, s1[15]));
   }
-  float mx = fmaxf(fmaxf(mx0, s0[15]), fmaxf(mx1, s1[15]));
   mx = fmaxf(mx, swap_halves(mx));   // the other 16 keys of each block for this query
   // The reference m_run only moves when a score exceeds it by more than
   // kLazyRescale, and at the first tile (which sets it from that tile's max).
@@ -486,7 +501,7 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] -= delta;
-      s1[r] -= delta;
+      if constexpr (!kHalf) s1[r] -= delta;
     }
     m_run += delta;
 #pragma unroll
@@ -498,7 +513,7 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
   for (int r = 0; r < 16; r += 2) exp_pair_shifted(s0, r, lsum, p0);
 
   // ---- O^T += Y^T P^T: step i covers block kb = i / 2DB, keys +16h (h = i / DB % 2), d-block b = i % DB
-  constexpr int NPV = 4 * DB;
+  constexpr int NPV = (kHalf ? 2 : 4) * DB;
   constexpr int AV = 2;                            // steps of value fragments in flight
   constexpr int EPS = 16 / (2 * DB);               // block-1 scores converted per block-0 step
   bf16x8_t yf[NPV];
@@ -519,7 +534,7 @@ __device__ __forceinline__ void stream_tile(const unsigned char *ks, const unsig
     const int kb = i / (2 * DB), h = (i / DB) & 1, b = i % DB;
     oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yf[i], kb ? p1[h] : p0[h], oacc[b], 0, 0, 0);
     if (i + AV < NPV) read_y(i + AV);
-    if (i < 2 * DB) {
+    if (!kHalf && i < 2 * DB) {
 #pragma unroll
       for (int e = 0; e < EPS; e += 2) exp_pair_shifted(s1, EPS * i + e, lsum, p1);
     }
@@ -729,8 +744,14 @@ __device__ __forceinline__ void stream_item(const AttnLaunch &p, uint32_t bid, u
       auto on_pv = [&](int i) __attribute__((always_inline)) {
         if (kDma && i % SP == 0 && i / SP < XP) window(kbytes, kn, kk0, (i / SP));
       };
-      stream_tile<D>(kc, yc, qb, t * kKeyTile, qhi, t == 0, negm, m_run, l_run, oacc, half, tr_col, lo,
-                     on_qk, on_pv);
+      if (!kDma && t * kKeyTile + 32 >= qhi && t > 0) {
+        // this wave's last tile holds at most 32 of its keys: block 0 only
+        stream_tile<D, true>(kc, yc, qb, t * kKeyTile, qhi, false, negm, m_run, l_run, oacc, half, tr_col, lo,
+                             on_qk, on_pv);
+      } else {
+        stream_tile<D>(kc, yc, qb, t * kKeyTile, qhi, t == 0, negm, m_run, l_run, oacc, half, tr_col, lo,
+                       on_qk, on_pv);
+      }
       if constexpr (kDma) {
 #pragma unroll
         for (int w = XP; w < WPT; ++w) window(kbytes, kn, kk0, w);
