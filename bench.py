@@ -91,8 +91,11 @@ def roofline_us(flops, nbytes):
 # The GPU's clocks ramp up over the first tens of milliseconds of work after an
 # idle period (0.245 ms/step after 10 warm-up steps against 0.232 after 200 on
 # one box): every timed loop is preceded by its --warmup steps and, when those
-# took less than this, by further untimed steps up to this much GPU time.
-MIN_WARM_MS = 50.0
+# took less than this, by further untimed steps up to this much time of steady
+# launches. The first call of a loop does not count: on a fresh process it also
+# loads code objects (tens of milliseconds of host time with an idle GPU; with it
+# counted, a 5-step warm-up ended with cold clocks and read 0.274 ms/step).
+MIN_WARM_MS = 80.0
 
 
 def time_loop(fn, steps, warmup, min_warm_ms=MIN_WARM_MS, info=None):
@@ -100,8 +103,11 @@ def time_loop(fn, steps, warmup, min_warm_ms=MIN_WARM_MS, info=None):
     untimed calls until at least min_warm_ms of warm-up have run; their count goes
     to info["extra_warmup"] when info is a dict)."""
     import torch
+    if warmup > 0 or min_warm_ms > 0:
+        fn(0)   # may load code objects: not part of the clock warm-up
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(warmup):
+    for i in range(1, warmup):
         fn(i)
     torch.cuda.synchronize()
     extra = 0
