@@ -60,3 +60,47 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
     assert out["bytes_per_launch"] == pytest.approx(out["fetch_bytes"] + out["write_bytes"])
     assert out["algorithmic_bytes"] == 8.0 * 32760 * 128 * 12
     assert os.path.exists(str(tmp_path / "t.json"))
+
+
+class _FakeEvent:
+    """Stands in for torch.cuda.Event on the host: elapsed_time in ms of wall clock."""
+
+    def __init__(self, enable_timing=True):
+        self.t = None
+
+    def record(self, stream=None):
+        import time
+        self.t = time.perf_counter()
+
+    def elapsed_time(self, other):
+        return (other.t - self.t) * 1e3
+
+
+def test_time_loop_warmup_does_not_count_the_first_call(monkeypatch):
+    """A slow first call (on a fresh process the first launch loads code objects) must not
+    stand in for the clock warm-up: steady calls still run until MIN_WARM_MS have passed."""
+    import time
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    monkeypatch.setattr(torch.cuda, "Event", _FakeEvent)
+    calls = []
+
+    def fn(i):
+        calls.append(i)
+        time.sleep(0.15 if len(calls) == 1 else 0.002)   # first call 150 ms, then 2 ms each
+
+    info = {}
+    bench.time_loop(fn, steps=3, warmup=2, min_warm_ms=40.0, info=info)
+    # about 40 ms / 2 ms of steady calls after the first one, in batches of 8
+    assert info["extra_warmup"] >= 8
+    steady = len(calls) - 3 - 1          # untimed calls after the first, timed calls excluded
+    assert steady * 2.0 >= 40.0 * 0.8    # they covered (nearly) the minimum warm-up time
+
+
+def test_repeat_stats_quantiles(monkeypatch):
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    monkeypatch.setattr(torch.cuda, "Event", _FakeEvent)
+    r = bench.repeat_stats(lambda i: None, steps=2, first_ms=5.0, repeats=3)
+    assert r["loops"] == 4 and r["steps_each"] == 2
+    assert r["p10_ms"] <= r["median_ms"] <= r["p90_ms"] <= 5.0
