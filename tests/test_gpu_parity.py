@@ -81,6 +81,22 @@ def test_small_bf16(grid, r_axes, tile, d):
     assert_bf16_parity(got, ref, "small bf16 %s r=%d tile=%s d=%d" % (grid, r_axes, tile, d))
 
 
+# Stage-L groups of T*H = 65, 80, 96 and 97 members: the last key tile holds 1, 16 and 32
+# keys (its second 32-key block is empty, so the streaming kernel runs that tile in its
+# half form) and 33 keys (the full form), at every head dim the streaming kernel serves.
+HALF_TILE_GRIDS = [(5, 13, 3), (4, 20, 3), (4, 24, 3), (1, 97, 3)]
+
+
+@pytest.mark.parametrize("d", [128, 64, 32, 16])
+@pytest.mark.parametrize("grid", HALF_TILE_GRIDS)
+def test_last_key_tile_boundary(grid, d):
+    q, k, v = _randn(grid, 2, d, seed=400 + d + grid[0] * grid[1])
+    got, _ = run_monarch(q, k, v, grid, "bf16", 1, None)
+    ref = oracle.monarch_attention(q, k, v, grid)
+    keys_in_last = grid[0] * grid[1] - 64
+    assert_bf16_parity(got, ref, "last key tile of %d keys %s d=%d" % (keys_in_last, grid, d))
+
+
 @pytest.mark.parametrize("d", [128, 64, 32, 16])
 @pytest.mark.parametrize("grid,r_axes,tile", SMALL)
 def test_small_f32(grid, r_axes, tile, d):
